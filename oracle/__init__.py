@@ -1,0 +1,13 @@
+"""CPU fp64 oracle for exact attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP library.
+"""
+
+from .exact import (  # noqa: F401
+    allowed_key_mask,
+    attention,
+    attention_head,
+    attention_rows,
+    attention_samples,
+)
