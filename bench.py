@@ -1,0 +1,248 @@
+"""Attention-forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-per-config] [--copy-calibration]
+
+One step is one exact-attention forward pass (every step of the method, one
+kernel launch) over one batch of the workload's synthetic inputs, already
+resident in device memory.  The default workload is the short-sequence batch
+(B=32, H=32, S=512, d=64, bf16, no mask: 16k tokens); all five workloads are
+also timed and reported under "per_config".  Rank 0 prints ONE JSON line.
+
+The timed region is bracketed by torch.cuda.synchronize(); the launches go on
+torch's current stream and are timed with HIP events recorded on that same
+stream.  The CPU baseline runs the fp64 oracle, untuned, on a bounded sample of
+the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_16_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_fa_fwd.md")
+
+
+def flops(w) -> float:
+    """Attention-forward FLOPs: 4 B H S^2 d, halved for the causal mask."""
+    f = 4.0 * w.B * w.H * w.S * w.S * w.d
+    return f / 2 if w.causal else f
+
+
+def algorithmic_bytes(w) -> int:
+    """Compulsory HBM bytes: read Q, K, V; write O (2 bytes each) and the fp32 LSE."""
+    n = w.B * w.H * w.S * w.d
+    return 4 * n * 2 + w.B * w.H * w.S * 4
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    for line in open(TRAFFIC_RECORD):
+        if line.startswith("traffic-record:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("workload") == workload and rec.get("kernel_sha") == kernel_hash():
+                return rec.get("bytes_per_launch")
+    return None
+
+
+def time_workload(w, steps: int, warmup: int):
+    import torch
+
+    import exact_attention_16_amd as fa
+    from exact_attention_16_amd.inputs import default_scale, make_inputs
+
+    q, k, v = (x.cuda() for x in make_inputs(w))
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=q.device)
+    scale = default_scale(w.d)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.forward(q, k, v, causal=w.causal, scale=scale, out=out, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    events[0].record(stream)
+    for i in range(steps):
+        fa.forward(q, k, v, causal=w.causal, scale=scale, out=out, lse=lse, stream=stream)
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [events[i].elapsed_time(events[i + 1]) for i in range(steps)]  # ms
+    total_ms = events[0].elapsed_time(events[-1])
+    ok = bool(torch.isfinite(lse).all().item())
+    del q, k, v, out, lse
+    return dict(total_ms=total_ms, per_ms=per, wall_s=wall, finite=ok)
+
+
+def cpu_baseline(w, budget_heads: int, min_seconds: float = 10.0):
+    """The fp64 oracle, as it stands, on the first `budget_heads` (b, h) heads."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_16_amd.inputs import default_scale, make_inputs
+
+    q, k, v = make_inputs(w)
+    n_heads = min(budget_heads, w.B * w.H)
+    b_n = max(1, n_heads // w.H)
+    h_n = w.H if n_heads >= w.H else n_heads
+    qs, ks, vs = (x[:b_n, :h_n].double().numpy() for x in (q, k, v))
+    try:
+        workers = len(os.sched_getaffinity(0))
+    except AttributeError:
+        workers = os.cpu_count() or 1
+    workers = max(1, min(workers, 16))
+    runs, t0 = 0, time.perf_counter()
+    while True:  # repeat the sample until about min_seconds of CPU work
+        o, l = oracle.attention(qs, ks, vs, w.causal, default_scale(w.d), workers=workers)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    sample = w.scaled(B=b_n, H=h_n)
+    return {
+        "value": runs * flops(sample) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{b_n * h_n} of {w.B * w.H} (b, h) heads of {w.name} (S={w.S}, d={w.d}), "
+                  f"fp64 numpy, {runs} run(s) in {dt:.1f} s wall",
+        "seconds": dt,
+    }
+
+
+def copy_calibration(steps: int):
+    """A plain 256 MiB device-to-device copy, for scaling the HBM counters."""
+    import torch
+
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return {"copy_bytes": n, "copies": steps}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="short_seq_batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1024)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the attention forward of each (batch, head) is "
+              "independent, and this build runs and reports the single-GPU path. "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_16_amd as fa
+    from exact_attention_16_amd.inputs import WORKLOADS, WORKLOADS_BY_NAME
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()  # fail loudly if the HIP library is missing
+
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(args.steps)), flush=True)
+        return
+
+    w = WORKLOADS_BY_NAME[args.workload]
+    torch.cuda.synchronize()
+    r = time_workload(w, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    ms = r["total_ms"] / args.steps
+    f = flops(w)
+    value = f / (ms * 1e-3) / 1e12
+    avg_launch_s = ms * 1e-3
+    ai = f / algorithmic_bytes(w)
+    bytes_pl = algorithmic_bytes(w)
+    if ai < RIDGE:
+        achieved = bytes_pl / avg_launch_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = f / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_TFLOPS}
+    roof["traffic"] = recorded_traffic(w.name)
+    roof["algorithmic_bytes"] = bytes_pl
+    roof["flops"] = f
+    roof["mfma_frac"] = value / PEAK_MFMA_TFLOPS
+    roof["kernel"] = "fa::detail::fwd_kernel"
+
+    per_config = []
+    if not args.no_per_config:
+        for wc in WORKLOADS:
+            steps = max(5, min(args.steps, int(2e9 / max(1.0, flops(wc) / 1e3))))
+            rc = time_workload(wc, steps, args.warmup)
+            msc = rc["total_ms"] / steps
+            tf = flops(wc) / (msc * 1e-3) / 1e12
+            per_config.append({"workload": wc.name, "B": wc.B, "H": wc.H, "S": wc.S, "d": wc.d,
+                               "dtype": wc.dtype, "causal": wc.causal, "ms": msc,
+                               "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MFMA_TFLOPS,
+                               "steps": steps, "finite": rc["finite"]})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_heads)
+
+    props = torch.cuda.get_device_properties(0)
+    line = {
+        "metric": "attention fwd TFLOPs/s and % of MI355X dense bf16 MFMA peak per config",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, rounded to the dtype)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "d": w.d,
+                   "causal": w.causal, "input_dtype": w.dtype, "tokens": w.B * w.S,
+                   "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_TFLOPS},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", "")},
+        "wall_s_timed_region": r["wall_s"],
+        "outputs_finite": r["finite"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

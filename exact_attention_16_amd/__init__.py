@@ -1,1 +1,19 @@
-"""MI355X-native exact-attention forward (FlashAttention-2 style) for gfx950."""
+"""MI355X-native exact-attention forward (FlashAttention-2 style) for gfx950.
+
+``forward(q, k, v, causal, scale) -> (o, lse)`` runs the HIP kernels of
+``libfa.so`` through its C ABI (include/fa.h).  The library is loaded on first
+use and its absence is an error.
+"""
+
+from .binding import (  # noqa: F401
+    FA_DTYPE_BF16,
+    FA_DTYPE_FP16,
+    FaError,
+    fa_fwd,
+    fa_last_hip_error,
+    fa_status_string,
+    fa_version,
+    forward,
+    library_path,
+    load_library,
+)

@@ -1,0 +1,88 @@
+// C-ABI front end of libfa.so: argument validation, status text and dispatch.
+// Validation runs on the host before any HIP call, so every error below can be
+// exercised without a GPU.
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+             int S, int d, int causal, float scale, int dtype) {
+  if (B < 0 || H < 0 || S < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  if ((long long)B * H * S == 0) return FA_OK;  // empty problem: nothing to touch
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
+  if ((long long)S * d >= (1LL << 30)) return FA_ERR_TOO_LARGE;  // 32-bit buffer offsets
+  fa::FwdArgs a{};
+  a.B = B; a.H = H; a.S = S; a.d = d;
+  if (fa::fwd_grid_size(a) > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+  const size_t nt = (size_t)B * H * S * d * 2;  // bytes of each of q, k, v, o
+  const size_t nl = (size_t)B * H * S * 4;      // bytes of lse
+  if (overlaps(o, nt, q, nt) || overlaps(o, nt, k, nt) || overlaps(o, nt, v, nt) ||
+      overlaps(o, nt, lse, nl) || overlaps(lse, nl, q, nt) || overlaps(lse, nl, k, nt) ||
+      overlaps(lse, nl, v, nt))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int d,
+           int causal, float scale, int dtype, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, H, S, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * S == 0) return FA_OK;
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.S = S; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.dtype = dtype;
+  const hipError_t e = fa::launch_fwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a pointer argument is NULL";
+    case FA_ERR_SHAPE: return "B, H or S is negative, or causal is not 0 or 1";
+    case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
+    case FA_ERR_SCALE: return "scale must be finite and >= 0";
+    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "o or lse overlaps an input, or o overlaps lse";
+    case FA_ERR_TOO_LARGE: return "problem too large: S*d must be < 2^30 and the grid < 2^31 work-groups";
+    case FA_ERR_HIP: return "the HIP runtime rejected the launch";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_hip_error(void) { return g_last_hip_error; }
+
+int fa_version(void) { return 100; }  // 0.1.0
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// Internal interface between the C-ABI front end (fa_api.cpp) and the gfx950
+// kernels (fa_fwd.hip).  Not installed; callers use include/fa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, S, d;
+  bool causal;
+  float scale;
+  int dtype;  // fa_dtype
+};
+
+// Number of work-groups the forward launch of `a` uses (for the host-side
+// grid-size check).  Requires a validated head dimension.
+long long fwd_grid_size(const FwdArgs& a);
+
+// Enqueue the forward kernels on `stream`; returns the launch status.
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+}  // namespace fa

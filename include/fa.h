@@ -1,0 +1,91 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library (libfa.so).
+ *
+ * The one operation is the FlashAttention-2 forward pass.  What it computes is
+ * exact attention (FlashAttention-2 abstract, searcharxiv abstract page,
+ * "Abstract": attention "with no approximation", in memory linear in the
+ * sequence length): for every batch b, head h and query row i
+ *
+ *     s_ij  = scale * <q_i, k_j>                 for keys j in A(i)
+ *     LSE_i = ln sum_{j in A(i)} exp(s_ij)         (natural log)
+ *     o_i   = sum_{j in A(i)} exp(s_ij - LSE_i) v_j
+ *
+ * with A(i) = {0..S-1}, or {0..i} when causal (query and key lengths are
+ * equal, so key j is kept iff j <= i).  It is computed tile by tile with an
+ * online softmax (IPLEX blog "FlashAttention-2: making long-context attention
+ * run efficiently on GPUs", section "Tiling preserves the attention
+ * calculation"), so the S x S score matrix never reaches device memory, and the
+ * result equals the definition up to floating-point rounding.  The per-row
+ * logsumexp is an output of this library; the pages do not mention it.
+ *
+ * All entry points are plain C: no HIP or torch types appear here.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o.  Accumulation is always fp32. */
+typedef enum { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
+
+/* Status codes returned by fa_fwd (0 = success, negative = error). */
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* a pointer argument is NULL (non-empty problem)       */
+  FA_ERR_SHAPE = -2,     /* B, H or S negative, or causal not 0/1                */
+  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128                                   */
+  FA_ERR_DTYPE = -4,     /* dtype is not an fa_dtype value                       */
+  FA_ERR_SCALE = -5,     /* scale is NaN, infinite or negative                   */
+  FA_ERR_ALIGN = -6,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte    */
+  FA_ERR_ALIAS = -7,     /* o or lse overlaps an input, or o overlaps lse        */
+  FA_ERR_TOO_LARGE = -8, /* S*d >= 2^30, or the launch grid would exceed 2^31-1  */
+  FA_ERR_HIP = -9        /* the HIP runtime rejected the launch (see below)      */
+};
+
+/*
+ * fa_fwd -- enqueue the exact-attention forward pass on `stream`.
+ *
+ * Arguments (all device pointers, caller-owned):
+ *   q, k, v  [B][H][S][d] dense row-major tensors of `dtype` (fp16 or bf16).
+ *   o        [B][H][S][d] dense row-major output of `dtype` (same as inputs).
+ *   lse      [B][H][S]    dense fp32 output: LSE_i, natural log, of the scaled
+ *                         and masked scores.
+ *   B, H, S  batch, heads, sequence length (query length = key length).
+ *            B*H*S == 0 is an empty problem: nothing is read or written and
+ *            FA_OK is returned (pointers may then be NULL).
+ *   d        head dimension: 64 or 128 (the pages' benchmark head sizes).
+ *   causal   0 = no mask; 1 = keep key j for query i iff j <= i.
+ *   scale    multiplies every score before the softmax; must be finite and
+ *            >= 0 (0 gives uniform weights).  Callers normally pass
+ *            1/sqrt(d) rounded to fp32.
+ *   dtype    an fa_dtype value.
+ *   stream   a hipStream_t passed as void*; NULL is the default stream.
+ *
+ * Behaviour: arguments are validated on the host before any HIP call; on a
+ * validation error nothing is enqueued.  The kernels are enqueued
+ * asynchronously and the call returns without synchronising.  The library
+ * allocates no device or host memory and keeps no state between calls, so it
+ * is reentrant and thread-safe.  Results are deterministic: each output element
+ * is written by exactly one thread, with no atomics.  On any error o and lse
+ * are left unspecified.  No exception or abort crosses this boundary.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int S, int d, int causal, float scale, int dtype,
+           void* stream);
+
+/* Static English text for a status code; never NULL. */
+const char* fa_status_string(int status);
+
+/* Text of the HIP error behind the calling thread's last FA_ERR_HIP; "" if none. */
+const char* fa_last_hip_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

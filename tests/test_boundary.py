@@ -1,0 +1,85 @@
+"""The C-ABI library on the CPU: it loads, exports what include/fa.h declares,
+and validates arguments before any HIP call (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_16_amd as fa
+from exact_attention_16_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from exact_attention_16_amd.build import build
+        build()
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_fwd", "fa_last_hip_error", "fa_status_string", "fa_version"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(binding.library_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), f"libfa.so does not export {name}"
+
+
+def test_status_strings(lib):
+    for st in range(-9, 1):
+        assert fa.fa_status_string(st)
+    assert fa.fa_status_string(12345) == "unknown status"
+    assert fa.fa_last_hip_error() == ""
+    assert fa.fa_version() >= 100
+
+
+# Fake, never-dereferenced device addresses: validation only looks at their
+# values.  Each buffer is 1 MiB apart so nothing overlaps unless a test wants it.
+BASE = 0x7F0000000000
+Q, K, V, O, L = (BASE + i * (1 << 20) for i in range(5))
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, S=64, d=64, causal=0, scale=0.125,
+            dtype=fa.FA_DTYPE_BF16)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"], a["d"],
+                     a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1), (dict(lse=0), -1),
+    (dict(B=-1), -2), (dict(H=-3), -2), (dict(S=-1), -2), (dict(causal=2), -2),
+    (dict(d=32), -3), (dict(d=96), -3), (dict(d=256), -3), (dict(d=0), -3),
+    (dict(dtype=2), -4), (dict(dtype=-1), -4),
+    (dict(scale=float("nan")), -5), (dict(scale=float("inf")), -5), (dict(scale=-0.5), -5),
+    (dict(q=Q + 8), -6), (dict(v=V + 2), -6), (dict(o=O + 4), -6), (dict(lse=L + 2), -6),
+    (dict(o=Q), -7), (dict(o=K + 64), -7), (dict(lse=V + 1024), -7), (dict(lse=O + 4096), -7),
+    (dict(S=1 << 23, d=128, q=BASE, k=BASE + (1 << 40), v=BASE + (2 << 40), o=BASE + (3 << 40),
+          lse=BASE + (4 << 40)), -8),
+])
+def test_validation_errors(lib, kw, status):
+    assert call(**kw) == status, fa.fa_status_string(status)
+
+
+def test_empty_problem_is_a_no_op(lib):
+    # B*H*S == 0: nothing is read or written, NULL pointers are fine
+    for dims in (dict(B=0), dict(H=0), dict(S=0)):
+        assert call(q=0, k=0, v=0, o=0, lse=0, **dims) == 0
+    # but the remaining arguments are still checked
+    assert call(S=0, d=48) == -3
+    assert call(S=0, scale=-1.0) == -5

@@ -1,0 +1,114 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+* small and medium shapes, compared element by element, spanning several
+  key and query tiles and ragged tails (S not a multiple of any tile size);
+* the five benchmark workloads at full size, in the same launch the benchmark
+  times: every output checked for finiteness and the value-hull property, one
+  whole head against the oracle, and sampled rows (tile boundaries, first and
+  last rows, random rows) of every head against the oracle one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_16_amd.inputs import (WORKLOADS, WORKLOADS_BY_NAME, Workload,
+                                           default_scale, make_inputs)
+from tests.gpu_helpers import TOL_LSE, TOL_O, check_full, gpu_forward, say, to64
+
+pytestmark = pytest.mark.gpu
+
+SEQ = [1, 2, 17, 63, 64, 65, 127, 128, 129, 255, 300, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("S", SEQ)
+def test_edge_lengths(S, d, causal, dtype):
+    w = Workload("edge", 1, 2, S, d, dtype, causal, seed=10_000 + S * 7 + d + causal)
+    q, k, v = make_inputs(w)
+    check_full(q, k, v, causal, default_scale(d), label=f"edge S={S}")
+
+
+@pytest.mark.parametrize("B,H,S,d,dtype,causal", [
+    (2, 3, 777, 128, "bf16", True),
+    (3, 2, 1029, 64, "fp16", False),
+    (1, 4, 2048, 128, "fp16", True),
+    (2, 2, 1536, 64, "bf16", True),
+    (1, 1, 4099, 128, "bf16", False),
+])
+def test_multi_tile_ragged(B, H, S, d, dtype, causal):
+    w = Workload("ragged", B, H, S, d, dtype, causal, seed=20_000 + S)
+    q, k, v = make_inputs(w)
+    check_full(q, k, v, causal, default_scale(d), label="ragged")
+
+
+def test_peaky_keys_medium():
+    """The long-sequence recipe (1 % of key rows x8) at a size the oracle
+    finishes in full."""
+    w = WORKLOADS_BY_NAME["long_seq_causal"].scaled(B=1, H=3, S=1500)
+    q, k, v = make_inputs(w)
+    check_full(q, k, v, True, default_scale(w.d), label="peaky")
+
+
+def test_tiny_workload_full():
+    w = WORKLOADS[0]
+    q, k, v = make_inputs(w)
+    eo, el = check_full(q, k, v, w.causal, default_scale(w.d), label=w.name)
+    print(f"tiny: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+
+
+def _sample_rows(S, rng, n_random):
+    fixed = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, S // 2, S - 2, S - 1}
+    rows = sorted(r for r in fixed if 0 <= r < S)
+    rows += rng.choice(S, size=min(S, n_random), replace=False).tolist()
+    return rows
+
+
+@pytest.mark.parametrize("name", [w.name for w in WORKLOADS[1:]])
+def test_full_size_workload(name):
+    w = WORKLOADS_BY_NAME[name]
+    scale = default_scale(w.d)
+    q, k, v = make_inputs(w)
+    say(f"workload {name} B={w.B} H={w.H} S={w.S} d={w.d} {w.dtype} causal={w.causal}")
+    o, lse = gpu_forward(q, k, v, w.causal, scale)
+
+    # properties over every output: finite; each O_i inside the per-head
+    # coordinatewise range of V (exact attention averages value rows)
+    assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
+    vd = v.cuda().float()
+    lo = vd.amin(dim=2, keepdim=True)
+    hi = vd.amax(dim=2, keepdim=True)
+    of = o.float()
+    margin = 0.05  # P is rounded to the input dtype before the PV product
+    assert bool(((of >= lo - margin) & (of <= hi + margin)).all().item())
+    del vd, lo, hi, of
+
+    o_cpu = o.float().cpu().double().numpy()
+    lse_cpu = lse.cpu().double().numpy()
+    del o, lse
+    qn, kn, vn = to64(q), to64(k), to64(v)
+
+    # one whole head
+    b0, h0 = w.B - 1, w.H // 2
+    oh, lh = oracle.attention_head(qn[b0, h0], kn[b0, h0], vn[b0, h0], w.causal, scale)
+    eo = float(np.abs(o_cpu[b0, h0] - oh).max())
+    el = float(np.abs(lse_cpu[b0, h0] - lh).max())
+    print(f"{name}: whole head ({b0},{h0}) max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE, (eo, el)
+
+    # sampled rows of (up to) 64 heads
+    rng = np.random.default_rng(w.seed)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if len(heads) > 64:
+        heads = [heads[i] for i in rng.choice(len(heads), size=64, replace=False)]
+    samples = [(b, h, i) for (b, h) in heads for i in _sample_rows(w.S, rng, 24)]
+    so, sl = oracle.attention_samples(qn, kn, vn, w.causal, scale, samples)
+    got_o = np.stack([o_cpu[b, h, i] for (b, h, i) in samples])
+    got_l = np.array([lse_cpu[b, h, i] for (b, h, i) in samples])
+    eo = float(np.abs(got_o - so).max())
+    el = float(np.abs(got_l - sl).max())
+    print(f"{name}: {len(samples)} sampled rows max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE, (eo, el)
