@@ -18,18 +18,25 @@
 //       tiles staged in LDS; each wavefront owns its rows' statistics and
 //       output outright, so nothing is reduced through LDS.
 //
-// MI355X mapping (own design, not the pages'): one wavefront owns 32 query
-// rows.  It computes the transposed score tile S^T = K Q^T with
-// v_mfma_f32_32x32x16_{bf16,f16} (A = K rows from LDS, B = Q rows held in
-// VGPRs), so every lane holds scores of ONE query: the row max and row sum are
-// in-lane, plus one exchange with lane l^32 (v_permlane32_swap).  The output
-// is accumulated transposed too, O^T += V^T P^T: B = P straight from the score
-// accumulator (no shuffle), A = V^T read with ds_read_b64_tr_b16 (gfx950's
-// transposing LDS read), and the per-row rescale and 1/l are per-lane scalars.
-// K and V tiles go HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
-// staging), double-buffered, XOR-swizzled in 16-byte chunks against LDS bank
-// conflicts; out-of-range rows read as zero and out-of-range stores are
-// dropped by the buffer descriptors' range checks.
+// MI355X mapping (own design, not the pages'):
+// * One wavefront owns 32 query rows.  It computes the transposed score tile
+//   S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16} (A = K from LDS, B = Q held
+//   in VGPRs), so each lane holds scores of ONE query: the row max and row sum
+//   are in-lane plus one exchange with lane l^32 (v_permlane32_swap).  The
+//   output is accumulated transposed too, O^T += V^T P^T: B = P straight from
+//   the score accumulator (no shuffle), A = V^T read with ds_read_b64_tr_b16
+//   (gfx950's transposing LDS read); the rescale and 1/l are per-lane scalars.
+// * Eight wavefronts per work-group (256 query rows), two per SIMD, in two
+//   groups of four that run half a tile out of phase ("ping-pong"): while one
+//   group's wavefront issues the MFMAs of P_{k-1} V_{k-1} and K_k Q^T, the
+//   other group's wavefront on the same SIMD runs the softmax of its tile, so
+//   the matrix cores and the vector ALUs work at the same time.  A work-group
+//   barrier separates the steps and keeps the groups one phase apart.
+// * K and V tiles go HBM -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//   staging), double-buffered, in a fragment-major layout that makes every
+//   LDS read linear and bank-conflict free.  Out-of-range rows read as zero
+//   and out-of-range stores are dropped by the buffer descriptors' range
+//   checks.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,6 +65,8 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // The partial output is rescaled only when a row max grows by more than this
 // many binary orders of magnitude, so unnormalised weights stay <= 2^8.
 constexpr float kRescaleMargin = 8.0f;
+// XCDs (each with its own L2) that work-groups are dealt to round-robin.
+constexpr int kXcds = 8;
 
 template <typename T>
 struct Elem;
@@ -98,20 +107,6 @@ struct Params {
   float c;     // scale * log2(e): scores enter exp2 as c * s
 };
 
-// XOR swizzle of the 16-byte chunk index inside a tile row, per tile.
-// K rows are read 16 B per lane (ds_read_b128) with 32 lanes on one logical
-// chunk of 32 consecutive rows; V rows are read 8 B per lane by the
-// transposing read, 4 rows x 64 B per half-wave.  Each swizzle spreads those
-// accesses over distinct 16-byte bank groups of a 256-byte bank row.
-template <int D>
-__device__ __forceinline__ int swz_k(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int row) {
-  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
@@ -134,14 +129,19 @@ __device__ __forceinline__ float max_with_partner(float x) { return fmaxf(x, par
 
 __device__ __forceinline__ float sum_with_partner(float x) { return x + partner_value(x); }
 
+// Work-group barrier without a memory fence: the waits each step needs are
+// explicit (s_waitcnt), and the "memory" clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // One wavefront's share of a work-group: 32 query rows of one (batch, head),
-// their Q fragments, running statistics and output accumulator.  The
-// work-group's NW wavefronts share the K/V tiles (BN keys each) in LDS.
-template <typename T, int D, bool CAUSAL, int NW, int BN>
+// their Q fragments, running statistics and output accumulator, plus the
+// score tile / weights of the key tile in flight.  The work-group's NW
+// wavefronts share the K/V tiles (BN keys each) in LDS.
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
 struct FwdWave {
   static constexpr int BM = NW * 32;
   static constexpr int ROW_BYTES = D * 2;
-  static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int KSTEPS = D / 16;    // MFMA k-steps of S^T over d
   static constexpr int DB = D / 32;        // 32-row blocks of O^T (over d)
   static constexpr int SB = BN / 32;       // 32-key blocks per tile
@@ -154,6 +154,7 @@ struct FwdWave {
   int qw;    // first query row of this wavefront
   int myq;   // the query row this lane holds
   int S;
+  int n;     // key tiles this work-group visits
   float c;   // scale * log2(e)
   const char* kh;
   const char* vh;
@@ -161,9 +162,14 @@ struct FwdWave {
 
   i16x8 qf[KSTEPS];
   f32x16 oacc[DB];
-  float m_used;  // reference max (raw score units) the weights are taken against
-  float mc;      // c * m_used
-  float lsum;    // this lane's share of the row sum
+  f32x16 sacc[SB];   // scores of the tile between its MFMA step and its softmax
+  i16x8 pf[SB][2];   // its weights between the softmax and the P V MFMAs
+  float m_used;      // reference max (raw score units) the weights are taken against
+  float mc;          // c * m_used
+  float lsum;        // this lane's share of the row sum
+
+  // Does this wavefront have any unmasked key in the tile starting at k0?
+  __device__ __forceinline__ bool active(int k0) const { return !(CAUSAL && k0 > qw + 31); }
 
   // Q rows -> VGPRs as the B operand of S^T = K Q^T (rows >= S read as 0).
   __device__ __forceinline__ void load_q(const char* qh) {
@@ -180,44 +186,110 @@ struct FwdWave {
     lsum = 0.f;
   }
 
-  // Start HBM -> LDS copies of key tile `tile` (K and V, BN rows each).  Each
-  // wave instruction fills 1 KiB of LDS in lane order; the lane picks the
-  // global 16-byte chunk that belongs at its swizzled slot.  Rows >= S read 0.
-  __device__ __forceinline__ void issue_tile(int tile, char* kd, char* vd) const {
+  // HBM -> LDS copies of one key tile (BN rows of K, or of V), issued
+  // cooperatively by all NW wavefronts.
+  //
+  // LDS holds each tile "fragment-major": every 1 KiB block is exactly what
+  // one wave instruction later reads, so every LDS read is a linear,
+  // bank-conflict-free access at lane * 16 (or lane * 8) plus an immediate.
+  // A direct-to-LDS buffer load also fills 1 KiB in lane order, so each lane
+  // simply fetches the global 16-byte chunk that belongs at its slot:
+  //   K block (sb, kk): lane l holds K[32*sb + l%32][16*kk + 8*(l/32) .. +8],
+  //     the A operand of one S^T MFMA;
+  //   V block (sb, cc, tt, dp): two 512-byte halves for d-blocks 2dp, 2dp+1;
+  //     in half x, bytes 8*l .. 8*l+8 are the 4 elements that lane l passes
+  //     to ds_read_b64_tr_b16 for the V^T operand of d-block 2dp+x, key
+  //     chunk (sb, cc), sub-step tt (see pv()).
+  // Rows >= S read as 0 (buffer range check).
+  __device__ __forceinline__ void issue_k(int tile, char* kd) const {
     const __amdgpu_buffer_rsrc_t rk = rsrc(kh, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = rsrc(vh, head_bytes);
+    const uint32_t base = (uint32_t)tile * BN * ROW_BYTES;
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      const int slot = (n * NW + wave) * 64 + lane;
-      const int row = slot / CPR;
-      const int pc = slot % CPR;
-      const uint32_t grow = (uint32_t)(tile * BN + row) * ROW_BYTES;
-      lds_void* dk = (lds_void*)(kd + (n * NW + wave) * 1024);
-      lds_void* dv = (lds_void*)(vd + (n * NW + wave) * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dk, 16, grow + ((pc ^ swz_k<D>(row)) << 4), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dv, 16, grow + ((pc ^ swz_v<D>(row)) << 4), 0, 0, 0);
+    for (int i = 0; i < LOADS; ++i) {
+      const int f = i * NW + wave;  // block (sb, kk)
+      const int ksb = f / KSTEPS, kk = f % KSTEPS;
+      const uint32_t off = base + (uint32_t)(ksb * 32 + (lane & 31)) * ROW_BYTES + (kk * 2 + (lane >> 5)) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + f * 1024), 16, off, 0, 0, 0);
     }
   }
 
-  // All of the online-softmax update for the key tile starting at k0.
-  __device__ __forceinline__ void compute_tile(int k0, const char* ks, const char* vs) {
-    // ---- S^T = K Q^T : lane holds 16 scores of query `myq` per 32-key block
-    f32x16 sacc[SB];
+  __device__ __forceinline__ void issue_v(int tile, char* vd) const {
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vh, head_bytes);
+    const uint32_t base = (uint32_t)tile * BN * ROW_BYTES;
+    const int x = lane >> 5;         // which half (d-block parity)
+    const int lp = lane & 31;
+    const int vg = lp >> 3;          // 16-lane group of the reading lanes 2lp, 2lp+1
+    const int vrow = (vg >> 1) * 4 + ((lp & 7) >> 1);
+    const int vcol = x * 32 + (vg & 1) * 16 + (lp & 1) * 8;
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      sacc[sb] = f32x16{};
-      const int row = sb * 32 + col;
+    for (int i = 0; i < LOADS; ++i) {
+      const int f = i * NW + wave;  // block ((sb * 2 + cc) * 2 + tt) * (DB / 2) + dp
+      const int dp = f % (DB / 2), rest = f / (DB / 2);
+      const uint32_t off = base + (uint32_t)(rest * 8 + vrow) * ROW_BYTES + (dp * 64 + vcol) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + f * 1024), 16, off, 0, 0, 0);
+    }
+  }
+
+  // S^T = K Q^T for the tile in `ks`: lane holds 16 scores of query `myq`
+  // per 32-key block (keys 8*(r/4) + 4*h + r%4 of the block, r = 0..15).
+  // The k-steps run in the outer loop so the SB accumulation chains
+  // interleave instead of waiting on one another.
+  __device__ __forceinline__ void scores(const char* ks) {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int pc = (kk * 2 + h) ^ swz_k<D>(row);
-        const i16x8 kf = *(const i16x8*)(ks + row * ROW_BYTES + pc * 16);
-        sacc[sb] = Elem<T>::mma(kf, qf[kk], sacc[sb]);
+    for (int sb = 0; sb < SB; ++sb) sacc[sb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      i16x8 kf[SB];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) kf[sb] = *(const i16x8*)(ks + (sb * KSTEPS + kk) * 1024 + lane * 16);
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) sacc[sb] = Elem<T>::mma(kf[sb], qf[kk], sacc[sb]);
+    }
+  }
+
+  // O^T += V^T P^T for the tile in `vs` and the weights in pf.  For chunk cc
+  // of 32-key block sb, MFMA k-index h*8 + 4*tt + e stands for key
+  // 32*sb + 16*cc + 8*tt + 4*h + e, matching where the score accumulator put
+  // that key's weight.  ds_read_b64_tr_b16 gives lane j of each 16-lane group
+  // element j%4 of the 8 bytes addressed by lanes 4e + j/4 of its group
+  // (e = 0..3); the V block layout puts there
+  // V[32*sb + 16*cc + 8*tt + 4*(g/2) + e][32*db + 16*(g%2) + j] for group g,
+  // i.e. lane l receives V^T[d = 32*db + l%32][its 4 keys].
+  __device__ __forceinline__ void pv(const char* vs) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          i16x4 half[2];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int blk = ((sb * 2 + cc) * 2 + tt) * (DB / 2) + (db >> 1);
+            const char* a = vs + blk * 1024 + (db & 1) * 512 + lane * 8;
+            half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
+          }
+          const i16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[db] = Elem<T>::mma(vf, pf[sb][cc], oacc[db]);
+        }
       }
     }
+  }
 
-    // ---- mask (only tiles crossing the diagonal or the sequence end)
-    const bool masked = (CAUSAL && k0 + BN - 1 > qw) || (k0 + BN > S);
-    if (masked) {
+  // Online-softmax update for the tile starting at k0 (scores in sacc):
+  // mask, row max, lazy rescale of O and l, weights P packed to T.  Only tiles
+  // that cross the causal diagonal or the sequence end are MASKED; the two
+  // variants are separate instantiations so the selects never run elsewhere.
+  __device__ __forceinline__ void softmax(int k0) {
+    if ((CAUSAL && k0 + BN - 1 > qw) || (TAIL && k0 + BN > S))
+      softmax_impl<true>(k0);
+    else
+      softmax_impl<false>(k0);
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void softmax_impl(int k0) {
+    if (MASKED) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
@@ -228,12 +300,18 @@ struct FwdWave {
         }
     }
 
-    // ---- online softmax statistics
-    float mx = -__builtin_inff();
+    // row max as a tree (independent max3 chains, then combined)
+    float mq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sacc[0][4 * j], sacc[0][4 * j + 1]);
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+      for (int r = 0; r < 16; r += 2) {
+        if (sb == 0 && (r & 3) == 0) continue;
+        mq[r >> 2] = fmaxf(mq[r >> 2], fmaxf(sacc[sb][r], sacc[sb][r + 1]));
+      }
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = max_with_partner(mx);
     const float m_new = fmaxf(m_used, mx);
     const bool grow = (m_used == -__builtin_inff()) || (c * (m_new - m_used) > kRescaleMargin);
@@ -247,16 +325,16 @@ struct FwdWave {
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
 
-    // ---- P = exp2(c s - c m), packed to T as the B operand of O^T += V^T P^T
-    i16x8 pf[SB][2];
+    // weights; the row sum is kept in four partial sums (independent chains)
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
       float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][r], c, -mc));
-        if (masked) e[r] = (sacc[sb][r] == -__builtin_inff()) ? 0.f : e[r];
-        lsum += e[r];
+        if (MASKED) e[r] = (sacc[sb][r] == -__builtin_inff()) ? 0.f : e[r];
+        ls[r & 3] += e[r];
       }
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -266,33 +344,20 @@ struct FwdWave {
         pf[sb][cc] = __builtin_bit_cast(i16x8, w);
       }
     }
+    lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  }
 
-    // ---- O^T += V^T P^T ; V^T fragments by transposing LDS reads.  For chunk
-    // cc of 32-key block sb, MFMA k-index h*8 + 4*tt + e stands for key
-    // 32*sb + 16*cc + 8*tt + 4*h + e, matching where the score accumulator
-    // put that key's weight in pf.
-    const int g = lane >> 4;  // 16-lane group
-    const int s16 = lane & 15;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          i16x4 half[2];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int row = sb * 32 + cc * 16 + tt * 8 + (g >> 1) * 4 + (s16 >> 2);
-            const int cv = db * 32 + (g & 1) * 16 + (s16 & 3) * 4;  // element column
-            const int pc = (cv >> 3) ^ swz_v<D>(row);
-            const char* a = vs + row * ROW_BYTES + pc * 16 + (cv & 7) * 2;
-            half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
-          }
-          const i16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = Elem<T>::mma(vf, pf[sb][cc], oacc[db]);
-        }
-      }
-    }
+  // Phase MFMA(k): P_{k-1} V_{k-1} (V from vp) and K_k Q^T (K from kc).
+  __device__ __forceinline__ void mfma_phase(int k, const char* kc, const char* vp) {
+    __builtin_amdgcn_s_setprio(1);
+    if (k >= 1 && active((k - 1) * BN)) pv(vp);
+    if (k < n && active(k * BN)) scores(kc);
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  // Phase SOFT(k): the softmax of tile k.
+  __device__ __forceinline__ void soft_phase(int k) {
+    if (k >= 0 && k < n && active(k * BN)) softmax(k * BN);
   }
 
   // O = O_acc / l and LSE = (c m + log2 l) ln 2; rows >= S are dropped by the
@@ -319,13 +384,30 @@ struct FwdWave {
   }
 };
 
-template <typename T, int D, bool CAUSAL, int NW, int BN>
+// TAIL: S is not a multiple of BN, so the last key tile needs the
+// sequence-end mask.
+//
+// Schedule.  With n key tiles, a wavefront's work is a sequence of phases:
+//   MFMA(0) = K_0 Q^T;  SOFT(k) = softmax of tile k;
+//   MFMA(k) = P_{k-1} V_{k-1} and K_k Q^T (k = 1..n; MFMA(n) is P V only).
+// The kernel runs 2n+2 barrier-separated steps.  Group 0 (wavefronts 0-3)
+// runs MFMA(k) in step 2k and SOFT(k) in step 2k+1; group 1 (wavefronts 4-7,
+// one per SIMD beside a group-0 wavefront) runs SOFT(k-1) in step 2k and
+// MFMA(k) in step 2k+1.  Loads: at the start of step 2k every wavefront
+// issues its share of K_{k+1} and V_k into the buffers that the barrier after
+// step 2k-1 has freed; they must land by step 2k+2, which the vmcnt(0) wait
+// before the barrier ending step 2k+1 guarantees.  K_k lives in K buffer k%2
+// and V_k in V buffer k%2.
+// One work-group per compute unit: two wavefronts per SIMD, at most 256
+// VGPRs each.
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(Params p) {
-  using W = FwdWave<T, D, CAUSAL, NW, BN>;
-  // Two stages of K and V tiles as four distinct LDS objects: the tile loop is
+  static_assert(NW == 8, "the ping-pong schedule pairs wavefronts w and w+4 on one SIMD");
+  using W = FwdWave<T, D, CAUSAL, TAIL, NW, BN>;
+  // K and V double buffers as four distinct LDS objects; the step loop is
   // unrolled by two so each access names its buffer at compile time, which
-  // lets the compiler see that reads of one stage never alias the
-  // direct-to-LDS loads filling the other (no spurious vmcnt waits).
+  // lets the compiler see that reads of one buffer never alias the
+  // direct-to-LDS loads filling another (no spurious vmcnt waits).
   __shared__ __attribute__((aligned(1024))) char k_lds0[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_lds1[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds0[W::TILE_BYTES];
@@ -336,13 +418,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(Params p) {
   w.wave = threadIdx.x >> 6;
   w.h = w.lane >> 5;
   w.col = w.lane & 31;
+  const int group = w.wave >> 2;
 
-  // Work-group -> (query block, head).  Consecutive ids walk the heads, so the
-  // query blocks of one head land on the same XCD when B*H is a multiple of 8
-  // (ids are dealt to the 8 XCDs round-robin) and share its L2.  Causal:
-  // the longest rows (most key tiles) are dispatched first.
-  const int bh = blockIdx.x % p.BH;
-  int qb = blockIdx.x / p.BH;
+  // Work-group -> (query block, head).  The dispatcher deals work-group ids
+  // to the chip's XCDs round-robin (id % kXcds), each XCD with its own L2.
+  // When B*H is a multiple of kXcds, the ids an XCD receives are remapped so
+  // that it runs all query blocks of one head back to back: they stream the
+  // same K/V tiles at about the same time, so each tile comes from HBM once
+  // per head.  Causal: within a head the longest query blocks (most key
+  // tiles) go first and the short ones fill the tail.
+  int bh, qb;
+  if (p.BH % kXcds == 0) {
+    const int local = blockIdx.x / kXcds;  // position in this XCD's queue
+    qb = local % p.nqb;
+    bh = (local / p.nqb) * kXcds + blockIdx.x % kXcds;
+  } else {
+    qb = blockIdx.x % p.nqb;
+    bh = blockIdx.x / p.nqb;
+  }
   if (CAUSAL) qb = p.nqb - 1 - qb;
   const int q_lo = qb * W::BM;
   w.qw = q_lo + w.wave * 32;
@@ -357,31 +450,39 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(Params p) {
   w.load_q((const char*)p.q + head_elems * 2);
 
   const int kv_end = CAUSAL ? min(p.S, q_lo + W::BM) : p.S;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  const int n = (kv_end + BN - 1) / BN;
+  w.n = n;
 
-  // Each step: wait for this tile's loads (own wave), barrier (everyone's
-  // loads landed, everyone done with the other stage), start the next tile's
-  // loads into the other stage, compute on this stage.
-  if (ntiles > 0) w.issue_tile(0, k_lds0, v_lds0);
-  for (int t = 0; t < ntiles; t += 2) {
+  w.issue_k(0, k_lds0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  barrier();
+
+  for (int k = 0; k <= n; k += 2) {
+    // ---- even k: K_k in buffer 0, V_{k-1} in buffer 1
+    if (k + 1 < n) w.issue_k(k + 1, k_lds1);
+    if (k < n) w.issue_v(k, v_lds0);
+    if (group == 0) w.mfma_phase(k, k_lds0, v_lds1); else w.soft_phase(k - 1);
+    barrier();
+    if (group == 0) w.soft_phase(k); else w.mfma_phase(k, k_lds0, v_lds1);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (t + 1 < ntiles) w.issue_tile(t + 1, k_lds1, v_lds1);
-    if (!(CAUSAL && t * BN > w.qw + 31)) w.compute_tile(t * BN, k_lds0, v_lds0);
-    if (t + 1 < ntiles) {
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      if (t + 2 < ntiles) w.issue_tile(t + 2, k_lds0, v_lds0);
-      if (!(CAUSAL && (t + 1) * BN > w.qw + 31)) w.compute_tile((t + 1) * BN, k_lds1, v_lds1);
-    }
+    barrier();
+    if (k + 1 > n) break;
+    // ---- odd k+1: K_{k+1} in buffer 1, V_k in buffer 0
+    if (k + 2 < n) w.issue_k(k + 2, k_lds0);
+    if (k + 1 < n) w.issue_v(k + 1, v_lds1);
+    if (group == 0) w.mfma_phase(k + 1, k_lds1, v_lds0); else w.soft_phase(k);
+    barrier();
+    if (group == 0) w.soft_phase(k + 1); else w.mfma_phase(k + 1, k_lds1, v_lds0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    barrier();
   }
   w.store(p.o, p.lse, head_elems, bh);
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kBN = 64;
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool TAIL>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = kWaves * 32;
   Params p;
@@ -395,15 +496,21 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.nqb = (a.S + BM - 1) / BM;
   p.c = a.scale * 1.4426950408889634f;
   const long long grid = (long long)p.nqb * p.BH;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, kWaves, kBN>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, kBN>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+  const bool tail = a.S % kBN != 0;
+  if (a.causal) return tail ? launch_t<T, D, true, true>(a, stream) : launch_t<T, D, true, false>(a, stream);
+  return tail ? launch_t<T, D, false, true>(a, stream) : launch_t<T, D, false, false>(a, stream);
+}
+
 template <typename T>
 hipError_t launch_dtype(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 64) return a.causal ? launch_t<T, 64, true>(a, stream) : launch_t<T, 64, false>(a, stream);
-  return a.causal ? launch_t<T, 128, true>(a, stream) : launch_t<T, 128, false>(a, stream);
+  return a.d == 64 ? launch_d<T, 64>(a, stream) : launch_d<T, 128>(a, stream);
 }
 
 }  // namespace detail
