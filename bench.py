@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
-KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_16_amd", "csrc", "fa_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_device.h")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_fa_fwd.md")
 
 
@@ -47,8 +48,12 @@ def algorithmic_bytes(w) -> int:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Identifies the kernel source the recorded HBM counters belong to."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):
@@ -157,8 +162,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the attention forward of each (batch, head) is "
-              "independent, and this build runs and reports the single-GPU path. "
+        print("bench.py measures one GPU only: the library runs the attention forward of one "
+              "GPU's share of (batch, head) pairs, and multi-GPU sharding is not implemented. "
               "Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -41,98 +41,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace detail {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(8))) short i16x8;
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Buffer descriptor word 3 for gfx9-family raw (untyped) buffers.
-constexpr int kRsrcWord3 = 0x00020000;
-// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima.
-constexpr int kWaitVmcnt0 = 0x0F70;
-// The partial output is rescaled only when a row max grows by more than this
-// many binary orders of magnitude, so unnormalised weights stay <= 2^8.
-constexpr float kRescaleMargin = 8.0f;
-// XCDs (each with its own L2) that work-groups are dealt to round-robin.
-constexpr int kXcds = 8;
-
-template <typename T>
-struct Elem;
-
-template <>
-struct Elem<__bf16> {
-  static __device__ __forceinline__ f32x16 mma(i16x8 a, i16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack(float x, float y) {
-    bf16x2 r = {(__bf16)x, (__bf16)y};
-    return __builtin_bit_cast(unsigned, r);
-  }
-};
-
-template <>
-struct Elem<_Float16> {
-  static __device__ __forceinline__ f32x16 mma(i16x8 a, i16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack(float x, float y) {
-    f16x2 r = {(_Float16)x, (_Float16)y};
-    return __builtin_bit_cast(unsigned, r);
-  }
-};
-
-struct Params {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* o;
-  float* lse;
-  int BH;      // B * H
-  int S;
-  int nqb;     // query-row blocks per head
-  float c;     // scale * log2(e): scores enter exp2 as c * s
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
-}
-
-// Value of x held by lane l^32.  v_permlane32_swap exchanges the upper half
-// of its first operand with the lower half of its second; called with two
-// copies of x, lanes 0-31 find the partner's value in the second result and
-// lanes 32-63 in the first.  The copy is made opaque because the compiler
-// otherwise folds the two identical operands and returns the first result
-// for both.
-__device__ __forceinline__ float partner_value(float x) {
-  float y;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                            __builtin_bit_cast(unsigned, y), false, false);
-  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
-}
-
-__device__ __forceinline__ float max_with_partner(float x) { return fmaxf(x, partner_value(x)); }
-
-__device__ __forceinline__ float sum_with_partner(float x) { return x + partner_value(x); }
-
-// Work-group barrier without a memory fence: the waits each step needs are
-// explicit (s_waitcnt), and the "memory" clobber keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // One wavefront's share of a work-group: 32 query rows of one (batch, head),
 // their Q fragments, running statistics and output accumulator, plus the
@@ -438,7 +351,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(Params p) {
   }
   if (CAUSAL) qb = p.nqb - 1 - qb;
   const int q_lo = qb * W::BM;
-  w.qw = q_lo + w.wave * 32;
+  // Row blocks alternate between the groups (group 0: blocks 0, 2, 4, 6;
+  // group 1: 1, 3, 5, 7), so near the causal diagonal both groups still have
+  // about the same number of key tiles and neither idles beside the other.
+  w.qw = q_lo + 32 * (2 * (w.wave & 3) + group);
   w.myq = w.qw + w.col;
   w.S = p.S;
   w.c = p.c;
@@ -480,7 +396,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(Params p) {
 }
 
 constexpr int kWaves = 8;
-constexpr int kBN = 64;
+// Keys per tile: 128 for d = 64 (halves the per-tile barrier and load-issue
+// overhead; the score tile still fits the register budget), 64 for d = 128.
+template <int D>
+constexpr int key_tile() { return D == 64 ? 128 : 64; }
 
 template <typename T, int D, bool CAUSAL, bool TAIL>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
@@ -496,14 +415,14 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.nqb = (a.S + BM - 1) / BM;
   p.c = a.scale * 1.4426950408889634f;
   const long long grid = (long long)p.nqb * p.BH;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, kBN>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, key_tile<D>()>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
                      stream, p);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  const bool tail = a.S % kBN != 0;
+  const bool tail = a.S % key_tile<D>() != 0;
   if (a.causal) return tail ? launch_t<T, D, true, true>(a, stream) : launch_t<T, D, true, false>(a, stream);
   return tail ? launch_t<T, D, false, true>(a, stream) : launch_t<T, D, false, false>(a, stream);
 }

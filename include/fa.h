@@ -3,8 +3,8 @@
  *
  * The one operation is the FlashAttention-2 forward pass.  What it computes is
  * exact attention (FlashAttention-2 abstract, searcharxiv abstract page,
- * "Abstract": attention "with no approximation", in memory linear in the
- * sequence length): for every batch b, head h and query row i
+ * "Abstract": attention computed exactly, in memory linear in the sequence
+ * length): for every batch b, head h and query row i
  *
  *     s_ij  = scale * <q_i, k_j>                 for keys j in A(i)
  *     LSE_i = ln sum_{j in A(i)} exp(s_ij)         (natural log)

@@ -8,9 +8,8 @@ helpers with the HIP library under ``exact_attention_16_amd/``.
 What it computes, and why it is the plain definition rather than a tiling:
 
 * FlashAttention-2 abstract (searcharxiv abstract page, "Abstract"): the method
-  computes attention "with no approximation"; the standard algorithm's runtime
-  and memory grow quadratically in the sequence length because it forms the
-  full score matrix.
+  computes attention exactly, without approximating it; the standard
+  algorithm's runtime and memory grow quadratically in the sequence length.
 * IPLEX blog "FlashAttention-2: making long-context attention run efficiently
   on GPUs", section "Tiling preserves the attention calculation": tiling with an
   online softmax is an exact-attention algorithm; it differs from the plain

@@ -7,9 +7,9 @@ case, hand-derived values, and invariants of exact attention.  The meta-test at
 the end plants plausible mistakes into the oracle's individual steps
 (monkeypatched, on the CPU) and requires every one of them to fail some pin.
 
-Definition pinned: exact attention ("no approximation", FlashAttention-2
-abstract, searcharxiv abstract page "Abstract"), with the logsumexp, causal
-alignment and scale readings stated in the oracle's header.
+Definition pinned: exact attention, computed without approximation
+(FlashAttention-2 abstract, searcharxiv abstract page "Abstract"), with the
+logsumexp, causal alignment and scale readings stated in the oracle's header.
 """
 
 import json

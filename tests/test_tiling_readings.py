@@ -2,10 +2,11 @@
 
 IPLEX blog "FlashAttention-2: making long-context attention run efficiently on
 GPUs", section "Tiling preserves the attention calculation":
-  * an online softmax that keeps running statistics and rescales the partial
-    outputs gives the globally normalised (exact) result;
-  * normalising each block on its own and adding the results is a different
-    calculation.
+  * an online softmax, which carries row statistics from block to block and
+    rescales the partial outputs accordingly, reproduces the exact softmax
+    over the whole row;
+  * a per-block softmax whose block results are simply summed computes
+    something else.
 
 Both statements are checked here with small float64 tilings written in this
 test (not in the oracle and not in the HIP library): the faithful tiling agrees
