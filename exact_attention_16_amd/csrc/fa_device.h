@@ -77,7 +77,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 // copies of x, lanes 0-31 find the partner's value in the second result and
 // lanes 32-63 in the first.  The copy is made opaque because the compiler
 // otherwise folds the two identical operands and returns the first result
-// for both.
+// for both.  The lane-half select is deliberate too: combining the two
+// results directly with a commutative operation (max or add of r[0] and
+// r[1]) is folded by this compiler into the operation of r[0] with itself.
 __device__ __forceinline__ float partner_value(float x) {
   float y;
   asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));

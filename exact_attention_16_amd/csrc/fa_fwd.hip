@@ -311,10 +311,17 @@ struct FwdWave {
 // step 2k-1 has freed; they must land by step 2k+2, which the vmcnt(0) wait
 // before the barrier ending step 2k+1 guarantees.  K_k lives in K buffer k%2
 // and V_k in V buffer k%2.
-// One work-group per compute unit: two wavefronts per SIMD, at most 256
-// VGPRs each.
+// Occupancy: head dimension 128 runs one work-group per compute unit (two
+// wavefronts per SIMD, at most 256 VGPRs each); head dimension 64 fits two
+// (at most 128 VGPRs each), so one work-group's prologue, barriers and
+// epilogue overlap the other's work.  The non-causal ragged-length variant
+// of d = 64 keeps one work-group per compute unit: its sequence-end mask
+// does not fit 128 VGPRs without spilling.
+template <int D, bool CAUSAL, bool TAIL>
+constexpr int waves_per_simd() { return (D == 64 && (CAUSAL || !TAIL)) ? 4 : 2; }
+
 template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void fwd_kernel(Params p) {
   static_assert(NW == 8, "the ping-pong schedule pairs wavefronts w and w+4 on one SIMD");
   using W = FwdWave<T, D, CAUSAL, TAIL, NW, BN>;
   // K and V double buffers as four distinct LDS objects; the step loop is
@@ -336,15 +343,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(Params p) {
   // Work-group -> (query block, head).  The dispatcher deals work-group ids
   // to the chip's XCDs round-robin (id % kXcds), each XCD with its own L2.
   // When B*H is a multiple of kXcds, the ids an XCD receives are remapped so
-  // that it runs all query blocks of one head back to back: they stream the
-  // same K/V tiles at about the same time, so each tile comes from HBM once
-  // per head.  Causal: within a head the longest query blocks (most key
-  // tiles) go first and the short ones fill the tail.
+  // that all of one head's query blocks run on one XCD.  Non-causal: an XCD
+  // runs a head's query blocks back to back; they stream the same K/V tiles
+  // at about the same time, so each tile comes from HBM once per head.
+  // Causal: query block qb visits qb + 1 row blocks' worth of key tiles, so
+  // an XCD's queue is ordered longest first across its heads (all heads'
+  // last query blocks, then the next-to-last, ...) and the short blocks fill
+  // the tail (greedy longest-processing-time scheduling).
   int bh, qb;
   if (p.BH % kXcds == 0) {
     const int local = blockIdx.x / kXcds;  // position in this XCD's queue
-    qb = local % p.nqb;
-    bh = (local / p.nqb) * kXcds + blockIdx.x % kXcds;
+    if (CAUSAL) {
+      const int heads_per_xcd = p.BH / kXcds;
+      qb = local / heads_per_xcd;
+      bh = (local % heads_per_xcd) * kXcds + blockIdx.x % kXcds;
+    } else {
+      qb = local % p.nqb;
+      bh = (local / p.nqb) * kXcds + blockIdx.x % kXcds;
+    }
   } else {
     qb = blockIdx.x % p.nqb;
     bh = blockIdx.x / p.nqb;
@@ -396,10 +412,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(Params p) {
 }
 
 constexpr int kWaves = 8;
-// Keys per tile: 128 for d = 64 (halves the per-tile barrier and load-issue
-// overhead; the score tile still fits the register budget), 64 for d = 128.
+// Keys per tile (chosen by measurement on the MI355X).
 template <int D>
-constexpr int key_tile() { return D == 64 ? 128 : 64; }
+constexpr int key_tile() { return 64; }
 
 template <typename T, int D, bool CAUSAL, bool TAIL>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {

@@ -53,6 +53,46 @@ def test_peaky_keys_medium():
     check_full(q, k, v, True, default_scale(w.d), label="peaky")
 
 
+def _level_inputs(shape, S, d, dtype, seed):
+    """q, k, v whose scores follow a chosen level L_j (in binary orders of
+    magnitude, c * s) along the key axis, plus noise of about one order.
+
+    q rows are 1 + 0.25 N(0,1) and key row j is t_j + 0.5 N(0,1) with
+    t_j = L_j / (log2(e) sqrt(d)), so with the default scale c * s_ij is about
+    L_j.  "rising" climbs 40 orders per 64 keys, "valley" falls by that much
+    and climbs back, "cliff" jumps by 300 orders (2^300 overflows fp32) at key
+    500.  Inputs are rounded to the dtype before anything sees them.
+    """
+    g = torch.Generator().manual_seed(seed)
+    j = torch.arange(S, dtype=torch.float64)
+    if shape == "rising":
+        level = 40.0 * torch.floor(j / 64)
+    elif shape == "valley":
+        level = 40.0 * torch.abs(torch.floor(j / 64) - 7)
+    else:
+        level = torch.where(j < 500, 0.0, 300.0)
+    t = level / (1.4426950408889634 * d ** 0.5)
+    q = 1.0 + 0.25 * torch.randn(1, 2, S, d, generator=g, dtype=torch.float64)
+    k = t[None, None, :, None] + 0.5 * torch.randn(1, 2, S, d, generator=g, dtype=torch.float64)
+    v = torch.randn(1, 2, S, d, generator=g, dtype=torch.float64)
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    return tuple(x.to(tdt) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("shape", ["rising", "valley", "cliff"])
+def test_moving_row_max(shape, d, causal, dtype):
+    """Row maxima that move by tens to hundreds of binary orders of magnitude
+    from tile to tile: the online softmax must move its reference max and
+    rescale the partial output many times (weights past the fp16 and bf16
+    bounds, and past fp32's range) and still match the oracle."""
+    S = 1000
+    q, k, v = _level_inputs(shape, S, d, dtype, seed=30_000 + 10 * d + causal)
+    check_full(q, k, v, causal, default_scale(d), label=f"level {shape}")
+
+
 def test_tiny_workload_full():
     w = WORKLOADS[0]
     q, k, v = make_inputs(w)
