@@ -1,13 +1,16 @@
 """Attention-forward benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--no-per-config] [--copy-calibration]
+                    [--no-cpu-baseline] [--no-per-config] [--no-sweep]
+                    [--copy-calibration]
 
 One step is one exact-attention forward pass (every step of the method, one
 kernel launch) over one batch of the workload's synthetic inputs, already
 resident in device memory.  The default workload is the short-sequence batch
 (B=32, H=32, S=512, d=64, bf16, no mask: 16k tokens); all five workloads are
-also timed and reported under "per_config".  Rank 0 prints ONE JSON line.
+also timed and reported under "per_config", and the pages' benchmark grid
+(S 512..16k x d 64/128 x causal, 16k tokens, bf16) under "sweep".  Rank 0
+prints ONE JSON line.
 
 The timed region is bracketed by torch.cuda.synchronize(); the launches go on
 torch's current stream and are timed with HIP events recorded on that same
@@ -158,6 +161,7 @@ def main():
     ap.add_argument("--workload", default="short_seq_batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the S x d x causal grid")
     ap.add_argument("--cpu-heads", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -171,7 +175,7 @@ def main():
     import torch
 
     import exact_attention_16_amd as fa
-    from exact_attention_16_amd.inputs import WORKLOADS, WORKLOADS_BY_NAME
+    from exact_attention_16_amd.inputs import SWEEP, WORKLOADS, WORKLOADS_BY_NAME
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -206,17 +210,23 @@ def main():
     roof["mfma_frac"] = value / PEAK_MFMA_TFLOPS
     roof["kernel"] = "fa::detail::fwd_kernel"
 
-    per_config = []
-    if not args.no_per_config:
-        for wc in WORKLOADS:
+    def time_list(workloads):
+        out = []
+        for wc in workloads:
             steps = max(5, min(args.steps, int(2e9 / max(1.0, flops(wc) / 1e3))))
             rc = time_workload(wc, steps, args.warmup)
             msc = rc["total_ms"] / steps
             tf = flops(wc) / (msc * 1e-3) / 1e12
-            per_config.append({"workload": wc.name, "B": wc.B, "H": wc.H, "S": wc.S, "d": wc.d,
-                               "dtype": wc.dtype, "causal": wc.causal, "ms": msc,
-                               "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MFMA_TFLOPS,
-                               "steps": steps, "finite": rc["finite"]})
+            out.append({"workload": wc.name, "B": wc.B, "H": wc.H, "S": wc.S, "d": wc.d,
+                        "dtype": wc.dtype, "causal": wc.causal, "ms": msc,
+                        "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MFMA_TFLOPS,
+                        "steps": steps, "finite": rc["finite"]})
+        return out
+
+    per_config = [] if args.no_per_config else time_list(WORKLOADS)
+    # The pages' kernel-benchmark grid (S 512..16k x d 64/128 x causal, 16k
+    # tokens per batch), bf16.
+    sweep = [] if args.no_sweep else time_list(SWEEP)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -242,6 +252,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "sweep": sweep,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
         "wall_s_timed_region": r["wall_s"],

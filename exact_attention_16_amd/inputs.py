@@ -31,7 +31,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "default_scale", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "SWEEP", "make_inputs", "default_scale", "torch_dtype"]
 
 
 @dataclass(frozen=True)
@@ -61,6 +61,18 @@ WORKLOADS = (
     Workload("single_seq_stress", 1, 32, 16384, 64, "fp16", False, 1005),
 )
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS}
+
+# The pages' kernel-benchmark grid (same blog section): S from 512 to 16k,
+# d in {64, 128}, causal off and on, 16k tokens per batch (B = 16384 / S).
+# The pages give no head count; H = 2048 / d (a 2048-wide model) is taken.
+# bf16 throughout; seeds 2001.. in grid order.
+SWEEP = tuple(
+    Workload(f"sweep_S{S}_d{d}_{'causal' if causal else 'full'}", 16384 // S, 2048 // d, S, d, "bf16", causal,
+             2001 + i)
+    for i, (S, d, causal) in enumerate(
+        (S, d, causal) for d in (64, 128) for causal in (False, True)
+        for S in (512, 1024, 2048, 4096, 8192, 16384)))
+SWEEP_BY_NAME = {w.name: w for w in SWEEP}
 
 
 def torch_dtype(name: str) -> torch.dtype:

@@ -5,7 +5,9 @@
 * the five benchmark workloads at full size, in the same launch the benchmark
   times: every output checked for finiteness and the value-hull property, one
   whole head against the oracle, and sampled rows (tile boundaries, first and
-  last rows, random rows) of every head against the oracle one by one.
+  last rows, random rows) of every head against the oracle one by one;
+* the 24 shapes of the pages' benchmark grid, in the launch the benchmark
+  times: finiteness and sampled rows of 8 heads.
 """
 
 import numpy as np
@@ -13,8 +15,8 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_16_amd.inputs import (WORKLOADS, WORKLOADS_BY_NAME, Workload,
-                                           default_scale, make_inputs)
+from exact_attention_16_amd.inputs import (SWEEP, SWEEP_BY_NAME, WORKLOADS, WORKLOADS_BY_NAME,
+                                           Workload, default_scale, make_inputs)
 from tests.gpu_helpers import TOL_LSE, TOL_O, check_full, gpu_forward, say, to64
 
 pytestmark = pytest.mark.gpu
@@ -146,6 +148,33 @@ def test_full_size_workload(name):
         heads = [heads[i] for i in rng.choice(len(heads), size=64, replace=False)]
     samples = [(b, h, i) for (b, h) in heads for i in _sample_rows(w.S, rng, 24)]
     so, sl = oracle.attention_samples(qn, kn, vn, w.causal, scale, samples)
+    got_o = np.stack([o_cpu[b, h, i] for (b, h, i) in samples])
+    got_l = np.array([lse_cpu[b, h, i] for (b, h, i) in samples])
+    eo = float(np.abs(got_o - so).max())
+    el = float(np.abs(got_l - sl).max())
+    print(f"{name}: {len(samples)} sampled rows max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE, (eo, el)
+
+
+@pytest.mark.parametrize("name", [w.name for w in SWEEP])
+def test_sweep_sampled(name):
+    """The pages' kernel-benchmark grid (S 512..16k x d 64/128 x causal, 16k
+    tokens per batch), in the launch the benchmark times: every output
+    finite, and sampled rows of 8 heads against the oracle one by one."""
+    w = SWEEP_BY_NAME[name]
+    scale = default_scale(w.d)
+    q, k, v = make_inputs(w)
+    say(f"sweep {name} B={w.B} H={w.H} S={w.S} d={w.d} causal={w.causal}")
+    o, lse = gpu_forward(q, k, v, w.causal, scale)
+    assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
+    o_cpu = o.float().cpu().double().numpy()
+    lse_cpu = lse.cpu().double().numpy()
+    del o, lse
+    rng = np.random.default_rng(w.seed)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    heads = [heads[i] for i in rng.choice(len(heads), size=min(8, len(heads)), replace=False)]
+    samples = [(b, h, i) for (b, h) in heads for i in _sample_rows(w.S, rng, 8)]
+    so, sl = oracle.attention_samples(to64(q), to64(k), to64(v), w.causal, scale, samples)
     got_o = np.stack([o_cpu[b, h, i] for (b, h, i) in samples])
     got_l = np.array([lse_cpu[b, h, i] for (b, h, i) in samples])
     eo = float(np.abs(got_o - so).max())
