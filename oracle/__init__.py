@@ -1,4 +1,4 @@
-"""CPU fp64 oracle for exact attention (test infrastructure only).
+"""CPU fp64 oracle for exact attention and its gradients (test infrastructure only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  It shares no code with the HIP library.
@@ -10,4 +10,9 @@ from .exact import (  # noqa: F401
     attention_head,
     attention_rows,
     attention_samples,
+)
+from .gradient import (  # noqa: F401
+    attention_backward,
+    attention_backward_head,
+    backward_samples,
 )
