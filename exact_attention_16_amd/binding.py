@@ -44,6 +44,8 @@ def load_library() -> ctypes.CDLL:
             vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
             lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
             lib.fa_fwd.restype = i
+            lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
+            lib.fa_bwd.restype = i
             lib.fa_status_string.argtypes = [i]
             lib.fa_status_string.restype = ctypes.c_char_p
             lib.fa_last_hip_error.argtypes = []
@@ -72,12 +74,18 @@ def fa_fwd(q, k, v, o, lse, B, H, S, d, causal, scale, dtype, stream) -> int:
                                       float(scale), int(dtype), stream))
 
 
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, stream) -> int:
+    """The C entry point with plain integers as pointers; returns the status."""
+    return int(load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, int(B), int(H), int(S), int(d),
+                                      int(causal), float(scale), int(dtype), stream))
+
+
 class FaError(RuntimeError):
-    def __init__(self, status: int):
+    def __init__(self, status: int, entry: str = "fa_fwd"):
         msg = fa_status_string(status)
         if status == FA_ERR_HIP:
             msg += f" ({fa_last_hip_error()})"
-        super().__init__(f"fa_fwd failed with status {status}: {msg}")
+        super().__init__(f"{entry} failed with status {status}: {msg}")
         self.status = status
 
 
@@ -115,3 +123,46 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if st != FA_OK:
         raise FaError(st)
     return out, lse
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, causal: bool = False, scale: float | None = None,
+             dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+             delta: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """Gradients (dq, dk, dv) of exact attention for the upstream gradient dout.
+
+    q, k, v, o, dout: [B, H, S, d] fp16/bf16 device tensors (o and lse from
+    ``forward`` on the same inputs, causal flag and scale); lse: [B, H, S]
+    float32.  ``delta`` is a [B, H, S] float32 scratch buffer the call fills
+    with D_i = dout_i . o_i (allocated here if not given).  Asynchronous on
+    ``stream`` (default: the current stream).
+    """
+    ts = (q, k, v, o, dout)
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o, dout must share one [B, H, S, d] shape")
+    if any(t.dtype != q.dtype for t in ts) or q.dtype not in _DTYPES:
+        raise TypeError("q, k, v, o, dout must all be float16 or all bfloat16")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts):
+        raise ValueError("q, k, v, o, dout must be contiguous device tensors")
+    B, H, S, d = q.shape
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
+    if scale is None:
+        scale = float(torch.tensor(d, dtype=torch.float32).rsqrt())
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if delta.shape != (B, H, S) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 [B, H, S] tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, S, d, 1 if causal else 0,
+                scale, _DTYPES[q.dtype], s.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -42,6 +42,44 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale,
+                 int dtype) {
+  if (B < 0 || H < 0 || S < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+  if ((long long)B * H * S == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3u) return FA_ERR_ALIGN;
+  if ((long long)S * d >= (1LL << 30)) return FA_ERR_TOO_LARGE;
+  fa::BwdArgs a{};
+  a.B = B; a.H = H; a.S = S; a.d = d;
+  if (fa::bwd_grid_size(a) > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+  const size_t nt = (size_t)B * H * S * d * 2;
+  const size_t nl = (size_t)B * H * S * 4;
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t in_bytes[6] = {nt, nt, nt, nt, nt, nl};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const size_t out_bytes[4] = {nt, nt, nt, nl};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FA_ERR_ALIAS;
+  }
+  return FA_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,12 +95,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.causal = causal != 0;
   a.scale = scale;
   a.dtype = dtype;
-  const hipError_t e = fa::launch_fwd(a, (hipStream_t)stream);
-  if (e != hipSuccess) {
-    snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
-    return FA_ERR_HIP;
-  }
-  return FA_OK;
+  return hip_status(fa::launch_fwd(a, (hipStream_t)stream));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale, int dtype,
+           void* stream) {
+  const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * S == 0) return FA_OK;
+  fa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.B = B; a.H = H; a.S = S; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.dtype = dtype;
+  return hip_status(fa::launch_bwd(a, (hipStream_t)stream));
 }
 
 const char* fa_status_string(int status) {
@@ -73,8 +122,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
-    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_ALIAS: return "o or lse overlaps an input, or o overlaps lse";
+    case FA_ERR_ALIGN: return "tensors must be 16-byte aligned, and lse and delta 4-byte aligned";
+    case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_TOO_LARGE: return "problem too large: S*d must be < 2^30 and the grid < 2^31 work-groups";
     case FA_ERR_HIP: return "the HIP runtime rejected the launch";
     default: return "unknown status";
@@ -83,6 +132,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_hip_error(void) { return g_last_hip_error; }
 
-int fa_version(void) { return 100; }  // 0.1.0
+int fa_version(void) { return 200; }  // 0.2.0
 
 }  // extern "C"

@@ -1,0 +1,620 @@
+// gfx950 (CDNA4) kernels of the exact-attention backward pass.
+//
+// The pages describe the method as exact attention used for training
+// (searcharxiv abstract page, "Abstract"), whose gradients match the plain
+// calculation up to rounding (IPLEX blog "FlashAttention-2: making long-context
+// attention run efficiently on GPUs", section "Tiling preserves the attention
+// calculation").  They do not give the backward algorithm; this is our own,
+// built from the chain rule of the forward definition and the same ideas the
+// pages credit for the forward pass: the S x S matrices never reach HBM (each
+// tile of P is recomputed from Q, K and the row logsumexp the forward pass
+// saved), work is spread over the sequence dimension as well as (batch, head)
+// (section "Three changes improve GPU utilisation"), and every wavefront owns
+// its accumulators outright, so nothing is reduced through LDS or atomics.
+//
+// With c = scale * log2(e), lse2_i = LSE_i * log2(e) and D_i = dO_i . O_i:
+//   P_ij  = 2^(c s_ij - lse2_i)        (s_ij = q_i . k_j; 0 for masked keys)
+//   dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dQ    = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+//
+// Two kernels, launched in this order on one stream:
+// * dq_kernel: one wavefront per 32 query rows (work-group = 8 wavefronts =
+//   256 rows, as in the forward pass).  It first computes D_i from dO and O
+//   and writes it to the caller's delta buffer, then walks the key tiles:
+//   S^T = K Q^T and dP^T = V dO^T on the matrix cores (Q and dO held in
+//   VGPRs, K and V from LDS), P, dS on the vector ALUs (each lane holds one
+//   query, so LSE_i and D_i are per-lane scalars), and dQ^T += K^T dS^T (K^T
+//   read through ds_read_b64_tr_b16).
+// * dkdv_kernel: one wavefront per 32 keys; K and V stay in VGPRs while the
+//   wavefront walks the query tiles: S = Q K^T and dP = dO V^T (each lane holds
+//   one key; LSE and D of the tile's queries come from LDS), then
+//   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+// Tiles move HBM -> LDS with direct-to-LDS buffer loads in the same
+// fragment-major layouts as the forward kernel, double-buffered.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace bwd {
+
+using namespace fa::detail;
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;
+  int BH;
+  int S;
+  int nblk;     // row blocks per head (query blocks for dq_kernel, key blocks for dkdv_kernel)
+  float scale;
+  float c;      // scale * log2(e)
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Tiles of ROWS rows x D columns, staged by NW wavefronts, in two LDS layouts:
+//   A layout: 1 KiB block (rb, kk) holds, at lane l, row 32 rb + l%32,
+//     columns 16 kk + 8 (l/32) .. +8: the A operand of a 32x32x16 MFMA whose
+//     m index is the row and whose k index is the column;
+//   T layout: the layout of the forward kernel's V tiles: two 512-byte halves
+//     per block ((rb*2 + cc)*2 + tt)*(DB/2) + dp, read with ds_read_b64_tr_b16
+//     into the A operand of an MFMA whose m index is the column (32 columns
+//     per d-block) and whose k index is the row (16 rows per chunk cc).
+template <int D, int NW, int ROWS>
+struct Tile {
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int RB = ROWS / 32;
+  static constexpr int BYTES = ROWS * ROW_BYTES;
+  static constexpr int LOADS = BYTES / (NW * 64 * 16);
+  static_assert(LOADS * NW * 64 * 16 == BYTES, "tile must split evenly over lanes");
+
+  static __device__ __forceinline__ void issue_a(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
+                                                 int lane) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int f = i * NW + wave;  // block (rb, kk)
+      const int rb = f / KSTEPS, kk = f % KSTEPS;
+      const uint32_t off = base + (uint32_t)(rb * 32 + (lane & 31)) * ROW_BYTES + (kk * 2 + (lane >> 5)) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + f * 1024), 16, off, 0, 0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ void issue_t(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
+                                                 int lane) {
+    const int x = lane >> 5;
+    const int lp = lane & 31;
+    const int vg = lp >> 3;
+    const int vrow = (vg >> 1) * 4 + ((lp & 7) >> 1);
+    const int vcol = x * 32 + (vg & 1) * 16 + (lp & 1) * 8;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int f = i * NW + wave;  // block ((rb * 2 + cc) * 2 + tt) * (DB / 2) + dp
+      const int dp = f % (DB / 2), rest = f / (DB / 2);
+      const uint32_t off = base + (uint32_t)(rest * 8 + vrow) * ROW_BYTES + (dp * 64 + vcol) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + f * 1024), 16, off, 0, 0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ i16x8 frag_a(const char* t, int rb, int kk, int lane) {
+    return *(const i16x8*)(t + (rb * KSTEPS + kk) * 1024 + lane * 16);
+  }
+
+  // A operand with m = columns 32 db .. +32 and k = rows 32 rb + 16 cc .. +16
+  // (row order permuted within the chunk exactly as a C-layout tile packed by
+  // pack_c puts it).
+  static __device__ __forceinline__ i16x8 frag_t(const char* t, int db, int rb, int cc, int lane) {
+    i16x4 half[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int blk = ((rb * 2 + cc) * 2 + tt) * (DB / 2) + (db >> 1);
+      half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + blk * 1024 + (db & 1) * 512 + lane * 8));
+    }
+    return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
+// Row fragments as the B operand (k = column, n = the lane's row): lane l
+// holds columns 16 kk + 8 (l/32) .. +8 of its row; rows past the range read 0.
+template <int D>
+__device__ __forceinline__ void load_row_frags(i16x8 (&f)[D / 16], const char* head, uint32_t head_bytes, int row,
+                                               int h) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(head, head_bytes);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint32_t off = (uint32_t)row * (D * 2) + (kk * 16 + h * 8) * 2;
+    f[kk] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float dot_pairs(i16x8 a, i16x8 b, float acc);
+
+// sum over the 8 element pairs of a . b, accumulated in fp32 (v_dot2).  Each
+// 32-bit word is copied to a scalar before its bit_cast: this compiler's
+// __builtin_bit_cast applied directly to a vector element (v[i]) reads
+// element 0 whatever the index.
+template <>
+__device__ __forceinline__ float dot_pairs<__bf16>(i16x8 a, i16x8 b, float acc) {
+  const u32x4 ua = __builtin_bit_cast(u32x4, a), ub = __builtin_bit_cast(u32x4, b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned xa = ua[i], xb = ub[i];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xa), __builtin_bit_cast(bf16x2, xb), acc, false);
+  }
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float dot_pairs<_Float16>(i16x8 a, i16x8 b, float acc) {
+  const u32x4 ua = __builtin_bit_cast(u32x4, a), ub = __builtin_bit_cast(u32x4, b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned xa = ua[i], xb = ub[i];
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, xa), __builtin_bit_cast(f16x2, xb), acc, false);
+  }
+  return acc;
+}
+
+// A C-layout 32x32 fp32 tile (16 values per lane) packed to T as the two B
+// operands (k chunks cc = 0, 1) of an MFMA whose k index is the tile's row:
+// value r of lane l sits at row 8 (r/4) + 4 (l/32) + r%4, and frag_t reads
+// the matching rows in the same order.
+template <typename T>
+__device__ __forceinline__ void pack_c(const float (&e)[16], i16x8 (&out)[2]) {
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = Elem<T>::pack(e[8 * cc + 2 * i], e[8 * cc + 2 * i + 1]);
+    out[cc] = __builtin_bit_cast(i16x8, w);
+  }
+}
+
+// Store a transposed C-layout accumulator set (acc[db] holds rows
+// 32 db + 8 (r/4) + 4 (l/32) + r%4 of the lane's output row's columns) times
+// `mul` as the lane's row of a row-major [rows x D] tensor in T.
+template <typename T, int D>
+__device__ __forceinline__ void store_row(const f32x16 (&acc)[D / 32], float mul, char* head, uint32_t head_bytes,
+                                          int row, int h) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(head, head_bytes);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      u32x2 w;
+      w[0] = Elem<T>::pack(acc[db][4 * rg + 0] * mul, acc[db][4 * rg + 1] * mul);
+      w[1] = Elem<T>::pack(acc[db][4 * rg + 2] * mul, acc[db][4 * rg + 3] * mul);
+      const int col = db * 32 + 8 * rg + 4 * h;
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, (uint32_t)row * (D * 2) + col * 2, 0, 0);
+    }
+}
+
+// Work-group -> (row block, head), dealing each head's row blocks to one XCD
+// (K/V or Q/dO tiles shared through that XCD's L2).  longest_first_reversed:
+// the causal dq blocks with the most key tiles are the LAST row blocks, the
+// causal dkdv blocks with the most query tiles are the FIRST; either way the
+// longest blocks of all heads on the XCD go first.
+__device__ __forceinline__ void map_block(int BH, int nblk, bool causal, bool last_is_longest, int& bh, int& blk) {
+  if (BH % kXcds == 0) {
+    const int local = blockIdx.x / kXcds;
+    if (causal) {
+      const int hpx = BH / kXcds;
+      blk = local / hpx;
+      bh = (local % hpx) * kXcds + blockIdx.x % kXcds;
+    } else {
+      blk = local % nblk;
+      bh = (local / nblk) * kXcds + blockIdx.x % kXcds;
+    }
+  } else {
+    blk = blockIdx.x % nblk;
+    bh = blockIdx.x / nblk;
+  }
+  if (causal && last_is_longest) blk = nblk - 1 - blk;
+}
+
+// ---------------------------------------------------------------- dQ kernel
+
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
+struct DqWave {
+  using KT = Tile<D, NW, BN>;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int SB = BN / 32;
+
+  int lane, h, qw, myq, S;
+  float c, lse2, dl;
+  i16x8 qf[KSTEPS], dof[KSTEPS];
+  f32x16 dq[DB];
+
+  __device__ __forceinline__ bool active(int k0) const { return !(CAUSAL && k0 > qw + 31); }
+  __device__ __forceinline__ bool masked(int k0) const {
+    return (CAUSAL && k0 + BN - 1 > qw) || (TAIL && k0 + BN > S);
+  }
+
+  // One key tile: kA = K (A layout), vA = V (A layout), kT = K (T layout).
+  template <bool MASKED>
+  __device__ __forceinline__ void step(const char* kA, const char* vA, const char* kT, int k0) {
+    f32x16 s[SB], dp[SB];
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) s[sb] = dp[sb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        s[sb] = Elem<T>::mma(KT::frag_a(kA, sb, kk, lane), qf[kk], s[sb]);
+        dp[sb] = Elem<T>::mma(KT::frag_a(vA, sb, kk, lane), dof[kk], dp[sb]);
+      }
+    }
+    i16x8 dsf[SB][2];
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -lse2));
+        if (MASKED) {
+          const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          p = (key < S && (!CAUSAL || key <= myq)) ? p : 0.f;
+        }
+        e[r] = p * (dp[sb][r] - dl);
+      }
+      pack_c<T>(e, dsf[sb]);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) dq[db] = Elem<T>::mma(KT::frag_t(kT, db, sb, cc, lane), dsf[sb][cc], dq[db]);
+  }
+};
+
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
+  using W = DqWave<T, D, CAUSAL, TAIL, NW, BN>;
+  using KT = typename W::KT;
+  constexpr int BM = NW * 32;
+  __shared__ __attribute__((aligned(1024))) char ka0[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char ka1[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char va0[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char va1[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kt0[KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kt1[KT::BYTES];
+
+  W w;
+  w.lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  w.h = w.lane >> 5;
+  int bh, qb;
+  map_block(p.BH, p.nblk, CAUSAL, true, bh, qb);
+  const int q_lo = qb * BM;
+  w.qw = q_lo + 32 * wave;
+  w.myq = w.qw + (w.lane & 31);
+  w.S = p.S;
+  w.c = p.c;
+
+  const size_t head_elems = (size_t)bh * p.S * D;
+  const uint32_t head_bytes = (uint32_t)p.S * D * 2;
+  const char* kh = (const char*)p.k + head_elems * 2;
+  const char* vh = (const char*)p.v + head_elems * 2;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vh, head_bytes);
+
+  // Q and dO rows of the lane's query; D_i = dO_i . O_i (each lane holds half
+  // the columns, its partner lane l^32 the other half); LSE_i in log2 units.
+  load_row_frags<D>(w.qf, (const char*)p.q + head_elems * 2, head_bytes, w.myq, w.h);
+  load_row_frags<D>(w.dof, (const char*)p.dout + head_elems * 2, head_bytes, w.myq, w.h);
+  {
+    i16x8 of[W::KSTEPS];
+    load_row_frags<D>(of, (const char*)p.o + head_elems * 2, head_bytes, w.myq, w.h);
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < W::KSTEPS; ++kk) part = dot_pairs<T>(w.dof[kk], of[kk], part);
+    w.dl = sum_with_partner(part);
+  }
+  const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (size_t)bh * p.S, (uint32_t)p.S * 4);
+  w.lse2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)w.myq * 4, 0, 0)) * kLog2e;
+  if (w.h == 0) {
+    const __amdgpu_buffer_rsrc_t rd = rsrc(p.delta + (size_t)bh * p.S, (uint32_t)p.S * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, w.dl), rd, (uint32_t)w.myq * 4, 0, 0);
+  }
+#pragma unroll
+  for (int db = 0; db < W::DB; ++db) w.dq[db] = f32x16{};
+
+  const int kv_end = CAUSAL ? min(p.S, q_lo + BM) : p.S;
+  const int n = (kv_end + BN - 1) / BN;
+  const uint32_t tb = (uint32_t)BN * D * 2;
+
+  KT::issue_a(rk, 0, ka0, wave, w.lane);
+  KT::issue_a(rv, 0, va0, wave, w.lane);
+  KT::issue_t(rk, 0, kt0, wave, w.lane);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  barrier();
+  for (int k = 0; k < n; k += 2) {
+    if (k + 1 < n) {
+      KT::issue_a(rk, (k + 1) * tb, ka1, wave, w.lane);
+      KT::issue_a(rv, (k + 1) * tb, va1, wave, w.lane);
+      KT::issue_t(rk, (k + 1) * tb, kt1, wave, w.lane);
+    }
+    if (w.active(k * BN)) {
+      if (w.masked(k * BN)) w.template step<true>(ka0, va0, kt0, k * BN);
+      else w.template step<false>(ka0, va0, kt0, k * BN);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    barrier();
+    if (k + 1 >= n) break;
+    if (k + 2 < n) {
+      KT::issue_a(rk, (k + 2) * tb, ka0, wave, w.lane);
+      KT::issue_a(rv, (k + 2) * tb, va0, wave, w.lane);
+      KT::issue_t(rk, (k + 2) * tb, kt0, wave, w.lane);
+    }
+    if (w.active((k + 1) * BN)) {
+      if (w.masked((k + 1) * BN)) w.template step<true>(ka1, va1, kt1, (k + 1) * BN);
+      else w.template step<false>(ka1, va1, kt1, (k + 1) * BN);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    barrier();
+  }
+  store_row<T, D>(w.dq, p.scale, (char*)p.dq + head_elems * 2, head_bytes, w.myq, w.h);
+}
+
+// ------------------------------------------------------------- dK/dV kernel
+
+// Floats reserved in LDS for a query tile's LSE values, and again for its D
+// values (one dword per lane of a wavefront).
+constexpr int kStatFloats = 64;
+
+template <typename T, int D, bool CAUSAL, int NW, int BQ>
+struct DkvWave {
+  using QT = Tile<D, NW, BQ>;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int QB = BQ / 32;
+
+  int lane, h, kw, myk;
+  float c;
+  i16x8 kf[KSTEPS], vf[KSTEPS];
+  f32x16 dk[DB], dv[DB];
+
+  __device__ __forceinline__ bool active(int q0) const { return !(CAUSAL && q0 + BQ - 1 < kw); }
+  __device__ __forceinline__ bool masked(int q0) const { return CAUSAL && q0 < kw + 31; }
+
+  // One query tile: qA, dA = Q, dO (A layout); qT, dT = Q, dO (T layout);
+  // st = the tile's LSE (floats 0..BQ-1) and D (floats kStatFloats..).
+  template <bool MASKED>
+  __device__ __forceinline__ void step(const char* qA, const char* dA, const char* qT, const char* dT,
+                                       const float* st, int q0) {
+    f32x16 s[QB], dp[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s[qb] = Elem<T>::mma(QT::frag_a(qA, qb, kk, lane), kf[kk], s[qb]);
+        dp[qb] = Elem<T>::mma(QT::frag_a(dA, qb, kk, lane), vf[kk], dp[qb]);
+      }
+    }
+    i16x8 pf[QB][2], dsf[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float pe[16], de[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // queries 32 qb + 8 j + 4 h + (0..3): four consecutive LSE and D values
+        const int qi = qb * 32 + 8 * j + 4 * h;
+        const float4 l4 = *(const float4*)(st + qi);
+        const float4 d4 = *(const float4*)(st + kStatFloats + qi);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * j + t;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c, -lv[t] * kLog2e));
+          if (MASKED) p = (q0 + qi + t >= myk) ? p : 0.f;
+          pe[r] = p;
+          de[r] = p * (dp[qb][r] - dvv[t]);
+        }
+      }
+      pack_c<T>(pe, pf[qb]);
+      pack_c<T>(de, dsf[qb]);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          dv[db] = Elem<T>::mma(QT::frag_t(dT, db, qb, cc, lane), pf[qb][cc], dv[db]);
+          dk[db] = Elem<T>::mma(QT::frag_t(qT, db, qb, cc, lane), dsf[qb][cc], dk[db]);
+        }
+  }
+};
+
+// LSE and D of a query tile into LDS (kStatFloats floats each): wavefront 0
+// fetches the LSE values, wavefront 1 the D values, one dword per lane, so
+// each writes 64 dwords; lanes >= BQ and rows past the sequence read 0.
+template <int BQ>
+__device__ __forceinline__ void issue_stats(__amdgpu_buffer_rsrc_t rl, __amdgpu_buffer_rsrc_t rd, int q0, char* dst,
+                                            int wave, int lane) {
+  static_assert(BQ <= kStatFloats, "one dword per lane");
+  const uint32_t off = (lane < BQ) ? (uint32_t)(q0 + lane) * 4 : 0x7FFFFFF0u;
+  if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)dst, 4, off, 0, 0, 0);
+  if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dst + kStatFloats * 4), 4, off, 0, 0, 0);
+}
+
+template <int D>
+constexpr int dkdv_waves() { return D == 64 ? 8 : 4; }
+
+template <typename T, int D, bool CAUSAL, int NW, int BQ>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParams p) {
+  using W = DkvWave<T, D, CAUSAL, NW, BQ>;
+  using QT = typename W::QT;
+  constexpr int BK = NW * 32;
+  __shared__ __attribute__((aligned(1024))) char qa0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qa1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char da0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char da1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qt0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qt1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char dt0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char dt1[QT::BYTES];
+  __shared__ __attribute__((aligned(16))) char st0[2 * kStatFloats * 4];
+  __shared__ __attribute__((aligned(16))) char st1[2 * kStatFloats * 4];
+
+  W w;
+  w.lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  w.h = w.lane >> 5;
+  int bh, kb;
+  map_block(p.BH, p.nblk, CAUSAL, false, bh, kb);
+  const int k_lo = kb * BK;
+  w.kw = k_lo + 32 * wave;
+  w.myk = w.kw + (w.lane & 31);
+  w.c = p.c;
+
+  const size_t head_elems = (size_t)bh * p.S * D;
+  const uint32_t head_bytes = (uint32_t)p.S * D * 2;
+  load_row_frags<D>(w.kf, (const char*)p.k + head_elems * 2, head_bytes, w.myk, w.h);
+  load_row_frags<D>(w.vf, (const char*)p.v + head_elems * 2, head_bytes, w.myk, w.h);
+#pragma unroll
+  for (int db = 0; db < W::DB; ++db) w.dk[db] = w.dv[db] = f32x16{};
+
+  const __amdgpu_buffer_rsrc_t rq = rsrc((const char*)p.q + head_elems * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = rsrc((const char*)p.dout + head_elems * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (size_t)bh * p.S, (uint32_t)p.S * 4);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(p.delta + (size_t)bh * p.S, (uint32_t)p.S * 4);
+
+  // query tiles t0 .. n-1 (causal: only queries >= the block's first key)
+  const int t0 = CAUSAL ? k_lo / BQ : 0;
+  const int n = (p.S + BQ - 1) / BQ;
+  const uint32_t tb = (uint32_t)BQ * D * 2;
+
+  if (t0 < n) {
+    QT::issue_a(rq, t0 * tb, qa0, wave, w.lane);
+    QT::issue_a(rdo, t0 * tb, da0, wave, w.lane);
+    QT::issue_t(rq, t0 * tb, qt0, wave, w.lane);
+    QT::issue_t(rdo, t0 * tb, dt0, wave, w.lane);
+    issue_stats<BQ>(rl, rd, t0 * BQ, st0, wave, w.lane);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  barrier();
+  for (int t = t0; t < n; t += 2) {
+    if (t + 1 < n) {
+      QT::issue_a(rq, (t + 1) * tb, qa1, wave, w.lane);
+      QT::issue_a(rdo, (t + 1) * tb, da1, wave, w.lane);
+      QT::issue_t(rq, (t + 1) * tb, qt1, wave, w.lane);
+      QT::issue_t(rdo, (t + 1) * tb, dt1, wave, w.lane);
+      issue_stats<BQ>(rl, rd, (t + 1) * BQ, st1, wave, w.lane);
+    }
+    if (w.active(t * BQ)) {
+      if (w.masked(t * BQ)) w.template step<true>(qa0, da0, qt0, dt0, (const float*)st0, t * BQ);
+      else w.template step<false>(qa0, da0, qt0, dt0, (const float*)st0, t * BQ);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    barrier();
+    if (t + 1 >= n) break;
+    if (t + 2 < n) {
+      QT::issue_a(rq, (t + 2) * tb, qa0, wave, w.lane);
+      QT::issue_a(rdo, (t + 2) * tb, da0, wave, w.lane);
+      QT::issue_t(rq, (t + 2) * tb, qt0, wave, w.lane);
+      QT::issue_t(rdo, (t + 2) * tb, dt0, wave, w.lane);
+      issue_stats<BQ>(rl, rd, (t + 2) * BQ, st0, wave, w.lane);
+    }
+    if (w.active((t + 1) * BQ)) {
+      if (w.masked((t + 1) * BQ)) w.template step<true>(qa1, da1, qt1, dt1, (const float*)st1, (t + 1) * BQ);
+      else w.template step<false>(qa1, da1, qt1, dt1, (const float*)st1, (t + 1) * BQ);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    barrier();
+  }
+  store_row<T, D>(w.dk, p.scale, (char*)p.dk + head_elems * 2, head_bytes, w.myk, w.h);
+  store_row<T, D>(w.dv, 1.0f, (char*)p.dv + head_elems * 2, head_bytes, w.myk, w.h);
+}
+
+// ------------------------------------------------------------------ launch
+
+constexpr int kDqWaves = 8;
+template <int D>
+constexpr int dq_key_tile() { return D == 64 ? 64 : 32; }
+template <int D>
+constexpr int dkdv_query_tile() { return D == 64 ? 64 : 32; }
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.dout = a.dout;
+  p.lse = a.lse;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.delta = a.delta;
+  p.BH = a.B * a.H;
+  p.S = a.S;
+  p.scale = a.scale;
+  p.c = a.scale * kLog2e;
+
+  constexpr int BM = kDqWaves * 32;
+  constexpr int BN = dq_key_tile<D>();
+  p.nblk = (a.S + BM - 1) / BM;
+  const bool tail = a.S % BN != 0;
+  if (tail)
+    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, true, kDqWaves, BN>), dim3((unsigned)(p.nblk * p.BH)),
+                       dim3(kDqWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, false, kDqWaves, BN>), dim3((unsigned)(p.nblk * p.BH)),
+                       dim3(kDqWaves * 64), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  constexpr int NW = dkdv_waves<D>();
+  constexpr int BK = NW * 32;
+  p.nblk = (a.S + BK - 1) / BK;
+  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, NW, dkdv_query_tile<D>()>), dim3((unsigned)(p.nblk * p.BH)),
+                     dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch_bwd_t<T, D, true>(a, stream) : launch_bwd_t<T, D, false>(a, stream);
+}
+
+template <typename T>
+hipError_t launch_bwd_dtype(const BwdArgs& a, hipStream_t stream) {
+  return a.d == 64 ? launch_bwd_d<T, 64>(a, stream) : launch_bwd_d<T, 128>(a, stream);
+}
+
+}  // namespace bwd
+
+long long bwd_grid_size(const BwdArgs& a) {
+  const long long bh = (long long)a.B * a.H;
+  const long long dq = (long long)((a.S + bwd::kDqWaves * 32 - 1) / (bwd::kDqWaves * 32)) * bh;
+  const int bk = (a.d == 64 ? bwd::dkdv_waves<64>() : bwd::dkdv_waves<128>()) * 32;
+  const long long dkdv = (long long)((a.S + bk - 1) / bk) * bh;
+  return dq > dkdv ? dq : dkdv;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  return a.dtype == 1 ? bwd::launch_bwd_dtype<__bf16>(a, stream) : bwd::launch_bwd_dtype<_Float16>(a, stream);
+}
+
+}  // namespace fa

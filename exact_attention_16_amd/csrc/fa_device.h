@@ -73,19 +73,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 
 // Value of x held by lane l^32.  v_permlane32_swap exchanges the upper half
-// of its first operand with the lower half of its second; called with two
-// copies of x, lanes 0-31 find the partner's value in the second result and
-// lanes 32-63 in the first.  The copy is made opaque because the compiler
-// otherwise folds the two identical operands and returns the first result
-// for both.  The lane-half select is deliberate too: combining the two
-// results directly with a commutative operation (max or add of r[0] and
-// r[1]) is folded by this compiler into the operation of r[0] with itself.
+// of its first operand with the lower half of its second; called with x
+// twice, lanes 0-31 find the partner's value in the second result and lanes
+// 32-63 in the first.  Each result element is copied to a scalar before use:
+// this compiler's __builtin_bit_cast applied directly to a vector element
+// (bit_cast(float, r[1])) reads element 0 whatever the index.  No inline
+// assembly is involved, so the compiler keeps the wait states that the
+// producer of x requires (a v_dot2 result, for one).
 __device__ __forceinline__ float partner_value(float x) {
-  float y;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                            __builtin_bit_cast(unsigned, y), false, false);
-  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+  const unsigned xb = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+  const unsigned lo = r[0], hi = r[1];
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? lo : hi);
 }
 
 __device__ __forceinline__ float max_with_partner(float x) { return fmaxf(x, partner_value(x)); }

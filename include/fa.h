@@ -1,7 +1,8 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library (libfa.so).
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
  *
- * The one operation is the FlashAttention-2 forward pass.  What it computes is
+ * The operations are the FlashAttention-2 forward pass (fa_fwd) and its
+ * gradients (fa_bwd).  What the forward pass computes is
  * exact attention (FlashAttention-2 abstract, searcharxiv abstract page,
  * "Abstract": attention computed exactly, in memory linear in the sequence
  * length): for every batch b, head h and query row i
@@ -30,7 +31,7 @@ extern "C" {
 /* Element type of q, k, v and o.  Accumulation is always fp32. */
 typedef enum { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
 
-/* Status codes returned by fa_fwd (0 = success, negative = error). */
+/* Status codes returned by fa_fwd and fa_bwd (0 = success, negative = error). */
 enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a pointer argument is NULL (non-empty problem)       */
@@ -38,8 +39,8 @@ enum {
   FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128                                   */
   FA_ERR_DTYPE = -4,     /* dtype is not an fa_dtype value                       */
   FA_ERR_SCALE = -5,     /* scale is NaN, infinite or negative                   */
-  FA_ERR_ALIGN = -6,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte    */
-  FA_ERR_ALIAS = -7,     /* o or lse overlaps an input, or o overlaps lse        */
+  FA_ERR_ALIGN = -6,     /* a tensor not 16-byte aligned, or lse/delta not 4-byte */
+  FA_ERR_ALIAS = -7,     /* an output overlaps an input or another output        */
   FA_ERR_TOO_LARGE = -8, /* S*d >= 2^30, or the launch grid would exceed 2^31-1  */
   FA_ERR_HIP = -9        /* the HIP runtime rejected the launch (see below)      */
 };
@@ -72,6 +73,48 @@ enum {
  * are left unspecified.  No exception or abort crosses this boundary.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int S, int d, int causal, float scale, int dtype,
+           void* stream);
+
+/*
+ * fa_bwd -- enqueue the gradients of the exact-attention forward pass.
+ *
+ * The pages state that the method trains GPT-style models (searcharxiv
+ * abstract page, "Abstract") and that its gradients match the plain
+ * calculation up to rounding (IPLEX blog, section "Tiling preserves the
+ * attention calculation"); they give no algorithm for them.  With dO the
+ * gradient of a scalar loss with respect to o, this computes the gradients of
+ * that loss with respect to q, k and v, per (b, h):
+ *
+ *     P_ij  = exp(s_ij - LSE_i) for j in A(i), 0 otherwise
+ *     dv    = P^T dO
+ *     D_i   = sum_c dO_ic o_ic
+ *     dS_ij = P_ij (dO_i . v_j - D_i)
+ *     dq    = scale * dS k,      dk = scale * dS^T q
+ *
+ * recomputing P tile by tile from q, k and the forward pass's LSE, so no
+ * S x S matrix reaches device memory.
+ *
+ * Arguments (all device pointers, caller-owned):
+ *   q, k, v     the forward pass's inputs, [B][H][S][d] of `dtype`.
+ *   o, lse      the forward pass's outputs for exactly these inputs, causal
+ *               flag and scale (o [B][H][S][d] of `dtype`, lse [B][H][S] fp32).
+ *   dout        dO, [B][H][S][d] of `dtype`.
+ *   dq, dk, dv  [B][H][S][d] outputs of `dtype`.
+ *   delta       [B][H][S] fp32 buffer the call writes D_i into (scratch that
+ *               the caller provides, so the library allocates nothing; its
+ *               contents on return are D_i).
+ *   B, H, S, d, causal, scale, dtype, stream: as for fa_fwd.
+ *
+ * Behaviour: as fa_fwd (host validation before any HIP call, asynchronous,
+ * no allocation, no state, deterministic: no atomics).  Two kernels are
+ * enqueued in order on `stream`: the first writes delta and dq, the second
+ * reads delta and writes dk and dv.  dq, dk, dv and delta must not overlap
+ * any input or each other (FA_ERR_ALIAS).  On any error the outputs are left
+ * unspecified.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int S, int d, int causal, float scale, int dtype,
            void* stream);
 

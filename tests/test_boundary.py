@@ -29,7 +29,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_fwd", "fa_last_hip_error", "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_last_hip_error", "fa_status_string", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -43,7 +43,7 @@ def test_status_strings(lib):
         assert fa.fa_status_string(st)
     assert fa.fa_status_string(12345) == "unknown status"
     assert fa.fa_last_hip_error() == ""
-    assert fa.fa_version() >= 100
+    assert fa.fa_version() >= 200
 
 
 # Fake, never-dereferenced device addresses: validation only looks at their
@@ -83,3 +83,38 @@ def test_empty_problem_is_a_no_op(lib):
     # but the remaining arguments are still checked
     assert call(S=0, d=48) == -3
     assert call(S=0, scale=-1.0) == -5
+
+
+# fa_bwd: ten buffers, each 1 MiB apart
+BQ_, BK_, BV_, BO_, BL_, BDO, BDQ, BDK, BDV, BDL = (BASE + (16 + i) * (1 << 20) for i in range(10))
+GOOD_BWD = dict(q=BQ_, k=BK_, v=BV_, o=BO_, lse=BL_, dout=BDO, dq=BDQ, dk=BDK, dv=BDV, delta=BDL,
+                B=1, H=2, S=64, d=64, causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16)
+
+
+def call_bwd(**kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["delta"],
+                     a["B"], a["H"], a["S"], a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(o=0), -1), (dict(lse=0), -1), (dict(dout=0), -1), (dict(dq=0), -1),
+    (dict(dk=0), -1), (dict(dv=0), -1), (dict(delta=0), -1),
+    (dict(B=-1), -2), (dict(causal=3), -2), (dict(d=80), -3), (dict(dtype=7), -4),
+    (dict(scale=float("nan")), -5), (dict(scale=-1.0), -5),
+    (dict(dout=BDO + 8), -6), (dict(dq=BDQ + 2), -6), (dict(delta=BDL + 2), -6), (dict(lse=BL_ + 1), -6),
+    (dict(dq=BQ_), -7), (dict(dk=BO_ + 64), -7), (dict(dv=BDO + 4096), -7), (dict(delta=BL_), -7),
+    (dict(dk=BDQ + 256), -7), (dict(delta=BDV + 16), -7), (dict(dq=BDL - 256), -7),
+    (dict(S=1 << 23, d=128, **{n: BASE + (i << 40) for i, n in enumerate(
+        ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta"))}), -8),
+])
+def test_backward_validation_errors(lib, kw, status):
+    assert call_bwd(**kw) == status, fa.fa_status_string(status)
+
+
+def test_backward_empty_problem_is_a_no_op(lib):
+    for dims in (dict(B=0), dict(H=0), dict(S=0)):
+        assert call_bwd(**{n: 0 for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")},
+                        **dims) == 0
+    assert call_bwd(S=0, d=48) == -3
