@@ -2,15 +2,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-per-config] [--no-sweep]
-                    [--copy-calibration]
+                    [--no-backward] [--copy-calibration]
 
 One step is one exact-attention forward pass (every step of the method, one
 kernel launch) over one batch of the workload's synthetic inputs, already
 resident in device memory.  The default workload is the short-sequence batch
 (B=32, H=32, S=512, d=64, bf16, no mask: 16k tokens); all five workloads are
-also timed and reported under "per_config", and the pages' benchmark grid
-(S 512..16k x d 64/128 x causal, 16k tokens, bf16) under "sweep".  Rank 0
-prints ONE JSON line.
+also timed and reported under "per_config", the pages' benchmark grid
+(S 512..16k x d 64/128 x causal, 16k tokens, bf16) under "sweep", and the
+gradients (fa_bwd) of the five workloads under "backward".  Rank 0 prints
+ONE JSON line.
 
 The timed region is bracketed by torch.cuda.synchronize(); the launches go on
 torch's current stream and are timed with HIP events recorded on that same
@@ -102,6 +103,37 @@ def time_workload(w, steps: int, warmup: int):
     return dict(total_ms=total_ms, wall_s=wall, finite=ok)
 
 
+def time_backward(w, steps: int, warmup: int):
+    """fa_bwd on the workload: inputs, o, lse, dO and every output buffer
+    resident in device memory before the timed region."""
+    import torch
+
+    import exact_attention_16_amd as fa
+    from exact_attention_16_amd.inputs import default_scale, make_inputs
+
+    q, k, v = (x.cuda() for x in make_inputs(w))
+    g = torch.Generator().manual_seed(w.seed + 777_777)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype).cuda()
+    scale = default_scale(w.d)
+    o, lse = fa.forward(q, k, v, causal=w.causal, scale=scale)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty_like(lse)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=scale, dq=dq, dk=dk, dv=dv, delta=delta,
+                    stream=stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fa.backward(q, k, v, o, lse, do, causal=w.causal, scale=scale, dq=dq, dk=dk, dv=dv, delta=delta,
+                    stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ok = all(bool(torch.isfinite(t.float()).all().item()) for t in (dq, dk, dv))
+    return dict(total_ms=start.elapsed_time(end), finite=ok)
+
+
 def cpu_baseline(w, budget_heads: int, min_seconds: float = 10.0):
     """The fp64 oracle, as it stands, on the first `budget_heads` (b, h) heads."""
     import numpy as np
@@ -162,6 +194,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the S x d x causal grid")
+    ap.add_argument("--no-backward", action="store_true", help="skip the gradient timings")
     ap.add_argument("--cpu-heads", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -224,6 +257,19 @@ def main():
         return out
 
     per_config = [] if args.no_per_config else time_list(WORKLOADS)
+    # Gradients of every workload (fa_bwd, two kernels per step).  FLOPs by
+    # the usual count for the attention backward: 2.5x the forward (five
+    # S x S x d products instead of two); the kernels recompute S and dP once
+    # more, which the count does not credit.
+    backward = []
+    if not args.no_backward:
+        for wc in WORKLOADS:
+            steps = max(5, min(args.steps, int(2e9 / max(1.0, 2.5 * flops(wc) / 1e3))))
+            rb = time_backward(wc, steps, args.warmup)
+            msb = rb["total_ms"] / steps
+            tf = 2.5 * flops(wc) / (msb * 1e-3) / 1e12
+            backward.append({"workload": wc.name, "ms": msb, "tflops": tf,
+                             "pct_peak": 100.0 * tf / PEAK_MFMA_TFLOPS, "steps": steps, "finite": rb["finite"]})
     # The pages' kernel-benchmark grid (S 512..16k x d 64/128 x causal, 16k
     # tokens per batch), bf16.
     sweep = [] if args.no_sweep else time_list(SWEEP)
@@ -253,6 +299,7 @@ def main():
         "cpu_baseline": cpu,
         "per_config": per_config,
         "sweep": sweep,
+        "backward": backward,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
         "wall_s_timed_region": r["wall_s"],
