@@ -16,3 +16,9 @@ from .gradient import (  # noqa: F401
     attention_backward_head,
     backward_samples,
 )
+from .kv import (  # noqa: F401
+    allowed_keys_kv,
+    attention_kv,
+    attention_kv_rows,
+    attention_kv_samples,
+)
