@@ -1,6 +1,7 @@
 """MI355X-native exact attention (FlashAttention-2 style) for gfx950.
 
-``forward(q, k, v, causal, scale) -> (o, lse)`` and
+``forward(q, k, v, causal, scale) -> (o, lse)`` (k, v may hold a different
+number of rows than q) and
 ``backward(q, k, v, o, lse, dout, causal, scale) -> (dq, dk, dv)`` run the HIP
 kernels of ``libfa.so`` through its C ABI (include/fa.h).  The library is
 loaded on first use and its absence is an error.
@@ -13,6 +14,7 @@ from .binding import (  # noqa: F401
     backward,
     fa_bwd,
     fa_fwd,
+    fa_fwd_kv,
     fa_last_hip_error,
     fa_status_string,
     fa_version,

@@ -44,6 +44,8 @@ def load_library() -> ctypes.CDLL:
             vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
             lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
             lib.fa_fwd.restype = i
+            lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+            lib.fa_fwd_kv.restype = i
             lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
             lib.fa_bwd.restype = i
             lib.fa_status_string.argtypes = [i]
@@ -74,6 +76,12 @@ def fa_fwd(q, k, v, o, lse, B, H, S, d, causal, scale, dtype, stream) -> int:
                                       float(scale), int(dtype), stream))
 
 
+def fa_fwd_kv(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, stream) -> int:
+    """The C entry point with plain integers as pointers; returns the status."""
+    return int(load_library().fa_fwd_kv(q, k, v, o, lse, int(B), int(H), int(Sq), int(Sk), int(d), int(causal),
+                                         float(scale), int(dtype), stream))
+
+
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, stream) -> int:
     """The C entry point with plain integers as pointers; returns the status."""
     return int(load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, int(B), int(H), int(S), int(d),
@@ -92,13 +100,17 @@ class FaError(RuntimeError):
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             scale: float | None = None, out: torch.Tensor | None = None,
             lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
-    """Exact attention forward on [B, H, S, d] fp16/bf16 device tensors.
+    """Exact attention forward on fp16/bf16 device tensors q [B, H, Sq, d] and
+    k, v [B, H, Sk, d].
 
-    Returns (o [B, H, S, d] in the input dtype, lse [B, H, S] float32).  The
-    launch is asynchronous on ``stream`` (default: the current stream).
+    Returns (o [B, H, Sq, d] in the input dtype, lse [B, H, Sq] float32).
+    With Sq != Sk this is fa_fwd_kv (causal mask aligned to the sequence
+    end), else fa_fwd.  The launch is asynchronous on ``stream`` (default:
+    the current stream).
     """
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError(f"q, k, v must share one [B, H, S, d] shape, got {tuple(q.shape)}, "
+    if (q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[:2] != q.shape[:2]
+            or k.shape[3] != q.shape[3]):
+        raise ValueError(f"need q [B, H, Sq, d] and k, v [B, H, Sk, d], got {tuple(q.shape)}, "
                          f"{tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
         raise TypeError("q, k, v must all be float16 or all bfloat16")
@@ -107,6 +119,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     B, H, S, d = q.shape
+    Sk = k.shape[2]
     if scale is None:
         scale = float(torch.tensor(d, dtype=torch.float32).rsqrt())
     if out is None:
@@ -118,10 +131,15 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, H, S, d, 1 if causal else 0, scale, _DTYPES[q.dtype], s.cuda_stream)
+    if Sk == S:
+        st, entry = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           B, H, S, d, 1 if causal else 0, scale, _DTYPES[q.dtype], s.cuda_stream), "fa_fwd"
+    else:
+        st, entry = fa_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              B, H, S, Sk, d, 1 if causal else 0, scale, _DTYPES[q.dtype],
+                              s.cuda_stream), "fa_fwd_kv"
     if st != FA_OK:
-        raise FaError(st)
+        raise FaError(st, entry)
     return out, lse
 
 

@@ -19,25 +19,28 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Shared by fa_fwd (Sk = S) and fa_fwd_kv.  With Sk = 0 the key tensors are
+// never read, so k and v may be NULL.
 int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
-             int S, int d, int causal, float scale, int dtype) {
-  if (B < 0 || H < 0 || S < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
+             int S, int Sk, int d, int causal, float scale, int dtype) {
+  if (B < 0 || H < 0 || S < 0 || Sk < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   if ((long long)B * H * S == 0) return FA_OK;  // empty problem: nothing to touch
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!q || !o || !lse || (Sk > 0 && (!k || !v))) return FA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
-  if ((long long)S * d >= (1LL << 30)) return FA_ERR_TOO_LARGE;  // 32-bit buffer offsets
+  if ((long long)S * d >= (1LL << 30) || (long long)Sk * d >= (1LL << 30)) return FA_ERR_TOO_LARGE;  // 32-bit buffer offsets
   fa::FwdArgs a{};
-  a.B = B; a.H = H; a.S = S; a.d = d;
+  a.B = B; a.H = H; a.S = S; a.Sk = Sk; a.d = d;
   if (fa::fwd_grid_size(a) > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
-  const size_t nt = (size_t)B * H * S * d * 2;  // bytes of each of q, k, v, o
-  const size_t nl = (size_t)B * H * S * 4;      // bytes of lse
-  if (overlaps(o, nt, q, nt) || overlaps(o, nt, k, nt) || overlaps(o, nt, v, nt) ||
-      overlaps(o, nt, lse, nl) || overlaps(lse, nl, q, nt) || overlaps(lse, nl, k, nt) ||
-      overlaps(lse, nl, v, nt))
+  const size_t nq = (size_t)B * H * S * d * 2;   // bytes of each of q, o
+  const size_t nk = (size_t)B * H * Sk * d * 2;  // bytes of each of k, v
+  const size_t nl = (size_t)B * H * S * 4;       // bytes of lse
+  if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nk) || overlaps(o, nq, v, nk) ||
+      overlaps(o, nq, lse, nl) || overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) ||
+      overlaps(lse, nl, v, nk))
     return FA_ERR_ALIAS;
   return FA_OK;
 }
@@ -80,22 +83,32 @@ int hip_status(hipError_t e) {
   return FA_ERR_HIP;
 }
 
+int forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int Sk, int d,
+            int causal, float scale, int dtype, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, H, S, Sk, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * S == 0) return FA_OK;
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.S = S; a.d = d; a.Sk = Sk;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.dtype = dtype;
+  return hip_status(fa::launch_fwd(a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int d,
            int causal, float scale, int dtype, void* stream) {
-  const int st = validate(q, k, v, o, lse, B, H, S, d, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  if ((long long)B * H * S == 0) return FA_OK;
-  fa::FwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.B = B; a.H = H; a.S = S; a.d = d;
-  a.causal = causal != 0;
-  a.scale = scale;
-  a.dtype = dtype;
-  return hip_status(fa::launch_fwd(a, (hipStream_t)stream));
+  return forward(q, k, v, o, lse, B, H, S, S, d, causal, scale, dtype, stream);
+}
+
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq, int Sk,
+              int d, int causal, float scale, int dtype, void* stream) {
+  return forward(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
@@ -118,13 +131,13 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a pointer argument is NULL";
-    case FA_ERR_SHAPE: return "B, H or S is negative, or causal is not 0 or 1";
+    case FA_ERR_SHAPE: return "B, H, S or Sk is negative, or causal is not 0 or 1";
     case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
     case FA_ERR_ALIGN: return "tensors must be 16-byte aligned, and lse and delta 4-byte aligned";
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
-    case FA_ERR_TOO_LARGE: return "problem too large: S*d must be < 2^30 and the grid < 2^31 work-groups";
+    case FA_ERR_TOO_LARGE: return "problem too large: S*d and Sk*d must be < 2^30 and the grid < 2^31 work-groups";
     case FA_ERR_HIP: return "the HIP runtime rejected the launch";
     default: return "unknown status";
   }
@@ -132,6 +145,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_hip_error(void) { return g_last_hip_error; }
 
-int fa_version(void) { return 200; }  // 0.2.0
+int fa_version(void) { return 300; }  // 0.3.0
 
 }  // extern "C"

@@ -63,7 +63,9 @@ struct Params {
   void* o;
   float* lse;
   int BH;      // B * H
-  int S;
+  int S;       // query rows per head
+  int Sk;      // key rows per head (= S for self-attention)
+  int shift;   // causal offset: query row i sits at key position i + shift (Sk - S)
   int nqb;     // query-row blocks per head
   float c;     // scale * log2(e): scores enter exp2 as c * s
 };

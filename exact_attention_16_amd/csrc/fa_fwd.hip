@@ -66,12 +66,15 @@ struct FwdWave {
   int lane, wave, h, col;
   int qw;    // first query row of this wavefront
   int myq;   // the query row this lane holds
-  int S;
+  int S;     // query rows
+  int Sk;    // key rows
+  int shift; // causal offset: key j is kept for query i iff j <= i + shift
   int n;     // key tiles this work-group visits
   float c;   // scale * log2(e)
   const char* kh;
   const char* vh;
-  uint32_t head_bytes;
+  uint32_t head_bytes;     // one head of q / o
+  uint32_t kv_head_bytes;  // one head of k / v
 
   i16x8 qf[KSTEPS];
   f32x16 oacc[DB];
@@ -82,7 +85,7 @@ struct FwdWave {
   float lsum;        // this lane's share of the row sum
 
   // Does this wavefront have any unmasked key in the tile starting at k0?
-  __device__ __forceinline__ bool active(int k0) const { return !(CAUSAL && k0 > qw + 31); }
+  __device__ __forceinline__ bool active(int k0) const { return !(CAUSAL && k0 > qw + 31 + shift); }
 
   // Q rows -> VGPRs as the B operand of S^T = K Q^T (rows >= S read as 0).
   __device__ __forceinline__ void load_q(const char* qh) {
@@ -115,7 +118,7 @@ struct FwdWave {
   //     chunk (sb, cc), sub-step tt (see pv()).
   // Rows >= S read as 0 (buffer range check).
   __device__ __forceinline__ void issue_k(int tile, char* kd) const {
-    const __amdgpu_buffer_rsrc_t rk = rsrc(kh, head_bytes);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kh, kv_head_bytes);
     const uint32_t base = (uint32_t)tile * BN * ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -127,7 +130,7 @@ struct FwdWave {
   }
 
   __device__ __forceinline__ void issue_v(int tile, char* vd) const {
-    const __amdgpu_buffer_rsrc_t rv = rsrc(vh, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vh, kv_head_bytes);
     const uint32_t base = (uint32_t)tile * BN * ROW_BYTES;
     const int x = lane >> 5;         // which half (d-block parity)
     const int lp = lane & 31;
@@ -194,7 +197,7 @@ struct FwdWave {
   // that cross the causal diagonal or the sequence end are MASKED; the two
   // variants are separate instantiations so the selects never run elsewhere.
   __device__ __forceinline__ void softmax(int k0) {
-    if ((CAUSAL && k0 + BN - 1 > qw) || (TAIL && k0 + BN > S))
+    if ((CAUSAL && k0 + BN - 1 > qw + shift) || (TAIL && k0 + BN > Sk))
       softmax_impl<true>(k0);
     else
       softmax_impl<false>(k0);
@@ -203,12 +206,17 @@ struct FwdWave {
   template <bool MASKED>
   __device__ __forceinline__ void softmax_impl(int k0) {
     if (MASKED) {
+      // key k0 + t + 4h (t below) is kept iff t < Sk - k0 - 4h and, when
+      // causal, t <= myq + shift - k0 - 4h
+      const int base = k0 + 4 * h;
+      const int end = Sk - base;
+      const int last = myq + shift - base;
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool ok = key < S && (!CAUSAL || key <= myq);
+          const int t = sb * 32 + 8 * (r >> 2) + (r & 3);
+          const bool ok = t < end && (!CAUSAL || t <= last);
           sacc[sb][r] = ok ? sacc[sb][r] : -__builtin_inff();
         }
     }
@@ -274,10 +282,12 @@ struct FwdWave {
   }
 
   // O = O_acc / l and LSE = (c m + log2 l) ln 2; rows >= S are dropped by the
-  // descriptors' range checks.
+  // descriptors' range checks.  A row that saw no key (causal, more query
+  // rows than keys) has l = 0: it stores O = 0 and LSE = -inf.
   __device__ __forceinline__ void store(void* o, float* lse, size_t head_elems, int bh) const {
     const float ltot = sum_with_partner(lsum);
-    const float inv = 1.0f / ltot;
+    const bool none = !(ltot > 0.f);
+    const float inv = none ? 0.f : 1.0f / ltot;
     const __amdgpu_buffer_rsrc_t ro = rsrc((const char*)o + head_elems * 2, head_bytes);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -291,14 +301,19 @@ struct FwdWave {
       }
     if (h == 0) {
       const __amdgpu_buffer_rsrc_t rl = rsrc(lse + (size_t)bh * S, (uint32_t)S * 4);
-      const float v = (mc + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f;
+      const float v = none ? -__builtin_inff() : (mc + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f;
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rl, (uint32_t)myq * 4, 0, 0);
     }
   }
 };
 
-// TAIL: S is not a multiple of BN, so the last key tile needs the
+// TAIL: Sk is not a multiple of BN, so the last key tile needs the
 // sequence-end mask.
+//
+// Separate lengths.  Q / O heads hold S rows and K / V heads Sk rows.  The
+// causal mask is aligned to the sequence end: query row i sits at key
+// position i + shift with shift = Sk - S, so with S = Sk it is the square
+// mask and a single query sees every key.
 //
 // Schedule.  With n key tiles, a wavefront's work is a sequence of phases:
 //   MFMA(0) = K_0 Q^T;  SOFT(k) = softmax of tile k;
@@ -373,16 +388,21 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
   w.qw = q_lo + 32 * (2 * (w.wave & 3) + group);
   w.myq = w.qw + w.col;
   w.S = p.S;
+  w.Sk = p.Sk;
+  w.shift = p.shift;
   w.c = p.c;
 
   const size_t head_elems = (size_t)bh * p.S * D;
+  const size_t kv_head_elems = (size_t)bh * p.Sk * D;
   w.head_bytes = (uint32_t)p.S * W::ROW_BYTES;
-  w.kh = (const char*)p.k + head_elems * 2;
-  w.vh = (const char*)p.v + head_elems * 2;
+  w.kv_head_bytes = (uint32_t)p.Sk * W::ROW_BYTES;
+  w.kh = (const char*)p.k + kv_head_elems * 2;
+  w.vh = (const char*)p.v + kv_head_elems * 2;
   w.load_q((const char*)p.q + head_elems * 2);
 
-  const int kv_end = CAUSAL ? min(p.S, q_lo + W::BM) : p.S;
-  const int n = (kv_end + BN - 1) / BN;
+  // keys this work-group visits (causal: up to its last row's position)
+  const int kv_end = CAUSAL ? min(p.Sk, q_lo + W::BM + p.shift) : p.Sk;
+  const int n = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   w.n = n;
 
   w.issue_k(0, k_lds0);
@@ -427,6 +447,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.lse = a.lse;
   p.BH = a.B * a.H;
   p.S = a.S;
+  p.Sk = a.Sk;
+  p.shift = a.causal ? a.Sk - a.S : 0;
   p.nqb = (a.S + BM - 1) / BM;
   p.c = a.scale * 1.4426950408889634f;
   const long long grid = (long long)p.nqb * p.BH;
@@ -437,7 +459,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
 
 template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  const bool tail = a.S % key_tile<D>() != 0;
+  const bool tail = a.Sk % key_tile<D>() != 0;
   if (a.causal) return tail ? launch_t<T, D, true, true>(a, stream) : launch_t<T, D, true, false>(a, stream);
   return tail ? launch_t<T, D, false, true>(a, stream) : launch_t<T, D, false, false>(a, stream);
 }

@@ -13,6 +13,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int B, H, S, d;
+  int Sk;     // key rows per head (= S for self-attention)
   bool causal;
   float scale;
   int dtype;  // fa_dtype

@@ -31,7 +31,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "SWEEP", "make_inputs", "default_scale", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "SWEEP", "make_inputs", "make_inputs_kv", "default_scale", "torch_dtype"]
 
 
 @dataclass(frozen=True)
@@ -107,4 +107,15 @@ def make_inputs(w: Workload, seed: int | None = None):
             for h in range(w.H):
                 k[b, h, rows[b, h]] *= w.peaky_mult
     dt = torch_dtype(w.dtype)
+    return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous()
+
+
+def make_inputs_kv(B: int, H: int, Sq: int, Sk: int, d: int, dtype: str, seed: int):
+    """(q [B, H, Sq, d], k, v [B, H, Sk, d]) by the same recipe as make_inputs:
+    i.i.d. N(0, 1) float32 drawn in the order Q, K, V, rounded to dtype."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, H, Sq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, Sk, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, Sk, d), generator=g, dtype=torch.float32)
+    dt = torch_dtype(dtype)
     return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous()

@@ -1,8 +1,8 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
  *
- * The operations are the FlashAttention-2 forward pass (fa_fwd) and its
- * gradients (fa_bwd).  What the forward pass computes is
+ * The operations are the FlashAttention-2 forward pass (fa_fwd, and
+ * fa_fwd_kv for separate query and key lengths) and its gradients (fa_bwd).  What the forward pass computes is
  * exact attention (FlashAttention-2 abstract, searcharxiv abstract page,
  * "Abstract": attention computed exactly, in memory linear in the sequence
  * length): for every batch b, head h and query row i
@@ -31,17 +31,17 @@ extern "C" {
 /* Element type of q, k, v and o.  Accumulation is always fp32. */
 typedef enum { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
 
-/* Status codes returned by fa_fwd and fa_bwd (0 = success, negative = error). */
+/* Status codes returned by the entry points (0 = success, negative = error). */
 enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a pointer argument is NULL (non-empty problem)       */
-  FA_ERR_SHAPE = -2,     /* B, H or S negative, or causal not 0/1                */
+  FA_ERR_SHAPE = -2,     /* B, H, S or Sk negative, or causal not 0/1            */
   FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128                                   */
   FA_ERR_DTYPE = -4,     /* dtype is not an fa_dtype value                       */
   FA_ERR_SCALE = -5,     /* scale is NaN, infinite or negative                   */
   FA_ERR_ALIGN = -6,     /* a tensor not 16-byte aligned, or lse/delta not 4-byte */
   FA_ERR_ALIAS = -7,     /* an output overlaps an input or another output        */
-  FA_ERR_TOO_LARGE = -8, /* S*d >= 2^30, or the launch grid would exceed 2^31-1  */
+  FA_ERR_TOO_LARGE = -8, /* S*d or Sk*d >= 2^30, or the grid exceeds 2^31-1      */
   FA_ERR_HIP = -9        /* the HIP runtime rejected the launch (see below)      */
 };
 
@@ -75,6 +75,35 @@ enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int S, int d, int causal, float scale, int dtype,
            void* stream);
+
+/*
+ * fa_fwd_kv -- fa_fwd with separate query and key lengths.
+ *
+ * The pages set the processing of a whole prompt apart from generating one
+ * token at a time, and say the two are bound differently (IPLEX blog
+ * "FlashAttention-2: making long-context attention run efficiently on GPUs",
+ * section "Document the implementation difference").  In generation the Sq
+ * new queries are the last Sq positions of a sequence whose first Sk
+ * positions carry the keys; the pages give no mask for this shape, and this
+ * library takes the end-aligned reading:
+ *
+ *     A(i) = {0..Sk-1}                       when causal = 0
+ *     A(i) = {j : j <= i + Sk - Sq}          when causal = 1
+ *
+ * so Sq = Sk is fa_fwd's square mask and a single query sees every key.  A
+ * row whose A(i) is empty (causal, Sq > Sk, rows i < Sq - Sk; or Sk = 0)
+ * gets o_i = 0 and LSE_i = -inf.
+ *
+ * Arguments: as for fa_fwd, except
+ *   q, o     [B][H][Sq][d];   lse [B][H][Sq];
+ *   k, v     [B][H][Sk][d]    (may be NULL when Sk == 0: never read);
+ *   Sq, Sk   query and key lengths, each >= 0 with Sq*d, Sk*d < 2^30.
+ * Behaviour, ownership and errors: as for fa_fwd.  fa_fwd_kv(..., S, S, ...)
+ * gives bitwise the same results as fa_fwd(..., S, ...).
+ */
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Sq, int Sk, int d, int causal, float scale,
+              int dtype, void* stream);
 
 /*
  * fa_bwd -- enqueue the gradients of the exact-attention forward pass.

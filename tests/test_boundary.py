@@ -29,7 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_last_hip_error", "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_kv", "fa_last_hip_error", "fa_status_string",
+                                   "fa_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -118,3 +119,34 @@ def test_backward_empty_problem_is_a_no_op(lib):
         assert call_bwd(**{n: 0 for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")},
                         **dims) == 0
     assert call_bwd(S=0, d=48) == -3
+
+
+# fa_fwd_kv: q, o, lse sized by Sq; k, v by Sk
+GOOD_KV = dict(GOOD, Sq=64, Sk=200)
+del GOOD_KV["S"]
+
+
+def call_kv(**kw):
+    a = dict(GOOD_KV)
+    a.update(kw)
+    return fa.fa_fwd_kv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Sq"], a["Sk"], a["d"],
+                        a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1), (dict(lse=0), -1),
+    (dict(Sq=-1), -2), (dict(Sk=-1), -2), (dict(causal=5), -2), (dict(d=96), -3), (dict(dtype=3), -4),
+    (dict(scale=float("inf")), -5), (dict(k=K + 8), -6), (dict(lse=L + 1), -6),
+    # k spans B*H*Sk*d*2 = 51200 bytes
+    (dict(o=K + 51184), -7), (dict(lse=V + 51196), -7), (dict(o=Q + 16), -7),
+    (dict(Sk=1 << 23, d=128, k=BASE + (1 << 40), v=BASE + (2 << 40)), -8),
+])
+def test_kv_validation_errors(lib, kw, status):
+    assert call_kv(**kw) == status, fa.fa_status_string(status)
+
+
+def test_kv_empty_problem_is_a_no_op(lib):
+    for dims in (dict(B=0), dict(H=0), dict(Sq=0)):
+        assert call_kv(q=0, k=0, v=0, o=0, lse=0, **dims) == 0
+    assert call_kv(Sq=0, d=48) == -3
+    assert call_kv(Sq=0, Sk=-2) == -2
