@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-per-config] [--no-sweep]
-                    [--no-backward] [--copy-calibration]
+                    [--no-backward] [--no-decode] [--copy-calibration]
 
 One step is one exact-attention forward pass (every step of the method, one
 kernel launch) over one batch of the workload's synthetic inputs, already
@@ -10,8 +10,9 @@ resident in device memory.  The default workload is the short-sequence batch
 (B=32, H=32, S=512, d=64, bf16, no mask: 16k tokens); all five workloads are
 also timed and reported under "per_config", the pages' benchmark grid
 (S 512..16k x d 64/128 x causal, 16k tokens, bf16) under "sweep", and the
-gradients (fa_bwd) of the five workloads under "backward".  Rank 0 prints
-ONE JSON line.
+gradients (fa_bwd) of the five workloads under "backward", and the split-key
+decoding pass (fa_fwd_decode) over three 1 GiB K/V caches under "decode".
+Rank 0 prints ONE JSON line.
 
 The timed region is bracketed by torch.cuda.synchronize(); the launches go on
 torch's current stream and are timed with HIP events recorded on that same
@@ -134,6 +135,41 @@ def time_backward(w, steps: int, warmup: int):
     return dict(total_ms=start.elapsed_time(end), finite=ok)
 
 
+def decode_bytes(w) -> int:
+    """Compulsory HBM bytes of a decoding call: read K and V (Sk rows) and Q,
+    write O (2 bytes each) and the fp32 LSE."""
+    return w.B * w.H * (2 * w.Sk * w.d * 2 + 2 * w.Sq * w.d * 2 + w.Sq * 4)
+
+
+def time_decode(w, steps: int, warmup: int):
+    """fa_fwd_decode (split pass + merge) with inputs, outputs and workspace
+    resident in device memory before the timed region."""
+    import torch
+
+    import exact_attention_16_amd as fa
+    from exact_attention_16_amd.inputs import default_scale
+
+    q, k, v = (x.cuda() for x in w.inputs())
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(16, fa.fa_fwd_decode_workspace_size(w.B, w.H, w.Sq, w.Sk, w.d)), dtype=torch.uint8,
+                     device=q.device)
+    scale = default_scale(w.d)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fa.decode(q, k, v, causal=w.causal, scale=scale, out=out, lse=lse, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fa.decode(q, k, v, causal=w.causal, scale=scale, out=out, lse=lse, workspace=ws, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ok = bool(torch.isfinite(lse).all().item()) and bool(torch.isfinite(out.float()).all().item())
+    del q, k, v
+    return dict(total_ms=start.elapsed_time(end), finite=ok, workspace_bytes=ws.numel())
+
+
 def cpu_baseline(w, budget_heads: int, min_seconds: float = 10.0):
     """The fp64 oracle, as it stands, on the first `budget_heads` (b, h) heads."""
     import numpy as np
@@ -195,6 +231,7 @@ def main():
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the S x d x causal grid")
     ap.add_argument("--no-backward", action="store_true", help="skip the gradient timings")
+    ap.add_argument("--no-decode", action="store_true", help="skip the split-key decoding timings")
     ap.add_argument("--cpu-heads", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -208,7 +245,7 @@ def main():
     import torch
 
     import exact_attention_16_amd as fa
-    from exact_attention_16_amd.inputs import SWEEP, WORKLOADS, WORKLOADS_BY_NAME
+    from exact_attention_16_amd.inputs import DECODE, SWEEP, WORKLOADS, WORKLOADS_BY_NAME
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -273,6 +310,19 @@ def main():
     # The pages' kernel-benchmark grid (S 512..16k x d 64/128 x causal, 16k
     # tokens per batch), bf16.
     sweep = [] if args.no_sweep else time_list(SWEEP)
+    # Token-by-token decoding (fa_fwd_decode: split pass + merge per step),
+    # bound by HBM: reported against the 8 TB/s peak.
+    decode = []
+    if not args.no_decode:
+        for wd in DECODE:
+            steps = max(10, args.steps)
+            rd = time_decode(wd, steps, args.warmup)
+            msd = rd["total_ms"] / steps
+            gbs = decode_bytes(wd) / (msd * 1e-3) / 1e9
+            decode.append({"workload": wd.name, "B": wd.B, "H": wd.H, "Sq": wd.Sq, "Sk": wd.Sk, "d": wd.d,
+                           "causal": wd.causal, "ms": msd, "algorithmic_bytes": decode_bytes(wd),
+                           "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "steps": steps,
+                           "workspace_bytes": rd["workspace_bytes"], "finite": rd["finite"]})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -300,6 +350,7 @@ def main():
         "per_config": per_config,
         "sweep": sweep,
         "backward": backward,
+        "decode": decode,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
         "wall_s_timed_region": r["wall_s"],

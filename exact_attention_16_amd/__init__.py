@@ -1,7 +1,8 @@
 """MI355X-native exact attention (FlashAttention-2 style) for gfx950.
 
 ``forward(q, k, v, causal, scale) -> (o, lse)`` (k, v may hold a different
-number of rows than q) and
+number of rows than q), ``decode(q, k, v, causal, scale) -> (o, lse)`` (the
+same split over the keys, for a few queries over many keys) and
 ``backward(q, k, v, o, lse, dout, causal, scale) -> (dq, dk, dv)`` run the HIP
 kernels of ``libfa.so`` through its C ABI (include/fa.h).  The library is
 loaded on first use and its absence is an error.
@@ -10,10 +11,14 @@ loaded on first use and its absence is an error.
 from .binding import (  # noqa: F401
     FA_DTYPE_BF16,
     FA_DTYPE_FP16,
+    FA_ERR_WORKSPACE,
     FaError,
     backward,
+    decode,
     fa_bwd,
     fa_fwd,
+    fa_fwd_decode,
+    fa_fwd_decode_workspace_size,
     fa_fwd_kv,
     fa_last_hip_error,
     fa_status_string,

@@ -19,6 +19,7 @@ FA_DTYPE_FP16 = 0
 FA_DTYPE_BF16 = 1
 FA_OK = 0
 FA_ERR_HIP = -9
+FA_ERR_WORKSPACE = -10
 
 _DTYPES = {torch.float16: FA_DTYPE_FP16, torch.bfloat16: FA_DTYPE_BF16}
 
@@ -46,6 +47,10 @@ def load_library() -> ctypes.CDLL:
             lib.fa_fwd.restype = i
             lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
             lib.fa_fwd_kv.restype = i
+            lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
+            lib.fa_fwd_decode.restype = i
+            lib.fa_fwd_decode_workspace_size.argtypes = [i, i, i, i, i]
+            lib.fa_fwd_decode_workspace_size.restype = ctypes.c_size_t
             lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
             lib.fa_bwd.restype = i
             lib.fa_status_string.argtypes = [i]
@@ -80,6 +85,17 @@ def fa_fwd_kv(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, stream) ->
     """The C entry point with plain integers as pointers; returns the status."""
     return int(load_library().fa_fwd_kv(q, k, v, o, lse, int(B), int(H), int(Sq), int(Sk), int(d), int(causal),
                                          float(scale), int(dtype), stream))
+
+
+def fa_fwd_decode(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, workspace, workspace_bytes,
+                  stream) -> int:
+    """The C entry point with plain integers as pointers; returns the status."""
+    return int(load_library().fa_fwd_decode(q, k, v, o, lse, int(B), int(H), int(Sq), int(Sk), int(d), int(causal),
+                                             float(scale), int(dtype), workspace, int(workspace_bytes), stream))
+
+
+def fa_fwd_decode_workspace_size(B, H, Sq, Sk, d) -> int:
+    return int(load_library().fa_fwd_decode_workspace_size(int(B), int(H), int(Sq), int(Sk), int(d)))
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, stream) -> int:
@@ -140,6 +156,48 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
                               s.cuda_stream), "fa_fwd_kv"
     if st != FA_OK:
         raise FaError(st, entry)
+    return out, lse
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+           scale: float | None = None, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
+    """fa_fwd_decode: q [B, H, Sq, d] (Sq small, e.g. 1) over k, v [B, H, Sk, d],
+    split over the keys.  Same results as ``forward`` to rounding.
+
+    ``workspace`` is a uint8 device tensor of at least
+    ``fa_fwd_decode_workspace_size(B, H, Sq, Sk, d)`` bytes (allocated here if
+    not given).  Returns (o, lse).  Asynchronous on ``stream``.
+    """
+    if (q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[:2] != q.shape[:2]
+            or k.shape[3] != q.shape[3]):
+        raise ValueError(f"need q [B, H, Sq, d] and k, v [B, H, Sk, d], got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must all be float16 or all bfloat16")
+    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    if scale is None:
+        scale = float(torch.tensor(d, dtype=torch.float32).rsqrt())
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+    need = fa_fwd_decode_workspace_size(B, H, Sq, Sk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Sq, Sk, d,
+                       1 if causal else 0, scale, _DTYPES[q.dtype], workspace.data_ptr(), nbytes, s.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_decode")
     return out, lse
 
 

@@ -77,6 +77,26 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   return FA_OK;
 }
 
+// fa_fwd_decode: validate() plus the workspace, which must be present, large
+// enough, 16-byte aligned and disjoint from every tensor.
+int validate_decode(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+                    int Sq, int Sk, int d, int causal, float scale, int dtype, const void* ws, size_t ws_bytes,
+                    fa::DecodePlan* plan) {
+  const int st = validate(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype);
+  if (st != FA_OK || (long long)B * H * Sq == 0) return st;
+  fa::DecodeArgs a{};
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  *plan = fa::decode_plan(a);
+  if (plan->grid > 0x7fffffffLL || (long long)B * H * Sq > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+  if (!ws || ws_bytes < plan->workspace_bytes || ((uintptr_t)ws & 15u)) return FA_ERR_WORKSPACE;
+  const size_t nq = (size_t)B * H * Sq * d * 2, nk = (size_t)B * H * Sk * d * 2, nl = (size_t)B * H * Sq * 4;
+  const size_t nw = plan->workspace_bytes;
+  if (overlaps(ws, nw, q, nq) || overlaps(ws, nw, k, nk) || overlaps(ws, nw, v, nk) || overlaps(ws, nw, o, nq) ||
+      overlaps(ws, nw, lse, nl))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
   snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
@@ -111,6 +131,29 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, 
   return forward(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, stream);
 }
 
+size_t fa_fwd_decode_workspace_size(int B, int H, int Sq, int Sk, int d) {
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk < 0 || (d != 64 && d != 128)) return 0;
+  fa::DecodeArgs a{};
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  return fa::decode_plan(a).workspace_bytes;
+}
+
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq, int Sk,
+                  int d, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  fa::DecodePlan plan{};
+  const int st = validate_decode(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, workspace,
+                                 workspace_bytes, &plan);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * Sq == 0) return FA_OK;
+  fa::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.workspace = workspace;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.dtype = dtype;
+  return hip_status(fa::launch_decode(a, plan, (hipStream_t)stream));
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale, int dtype,
            void* stream) {
@@ -139,6 +182,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIAS: return "an output overlaps an input or another output";
     case FA_ERR_TOO_LARGE: return "problem too large: S*d and Sk*d must be < 2^30 and the grid < 2^31 work-groups";
     case FA_ERR_HIP: return "the HIP runtime rejected the launch";
+    case FA_ERR_WORKSPACE:
+      return "workspace is NULL, smaller than fa_fwd_decode_workspace_size() or not 16-byte aligned";
     default: return "unknown status";
   }
 }

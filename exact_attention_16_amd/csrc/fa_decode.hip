@@ -1,0 +1,247 @@
+// gfx950 kernels of the split-key forward pass for short query blocks
+// (token-by-token decoding).
+//
+// The pages set decoding apart from the processing of a whole prompt: the two
+// are bound by different things (IPLEX blog "FlashAttention-2: making
+// long-context attention run efficiently on GPUs", section "Document the
+// implementation difference").  With a handful of new queries over a long
+// key sequence there is almost no arithmetic per byte of K and V (about Sq
+// flops per byte), so the pass is bound by HBM bandwidth, and the prefill
+// grid of one work-group per 256-row query block and head leaves most of the
+// chip idle.  This path therefore also splits the KEYS, which is the
+// FlashAttention-2 "sequence parallelism" applied to the other sequence axis:
+//
+// * decode_kernel: work-group = (head, 32-row query block, key split).  Its
+//   NW wavefronts load shared tiles of 32*NW keys HBM -> LDS with
+//   buffer_load ... lds; wavefront w takes 32-key block w of each tile and
+//   keeps its own online softmax over the keys it saw (the same MFMA score /
+//   output products and softmax as the prefill kernel).  Each
+//   wavefront writes its normalised partial output and partial LSE (fp32) to
+//   a caller-provided workspace: no atomics, no reduction through LDS.
+// * merge_kernel: one wavefront per (head, query row) combines the P
+//   partials exactly: LSE = ln sum_p exp(LSE_p) and O = sum_p exp(LSE_p - LSE)
+//   O_p.  Partials of key subsets a row cannot see have LSE_p = -inf and drop
+//   out; a row that sees no key at all gets O = 0, LSE = -inf.
+//
+// The key subsets of the partials are disjoint and cover every key, so the
+// merge gives the whole softmax: softmax over a union of disjoint sets is the
+// LSE-weighted mix of the per-set softmaxes.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_fwd_wave.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace detail {
+
+struct DecParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* po;        // partial outputs [BH][P][Sq][D]
+  float* pl;        // partial LSEs    [BH][P][Sq]
+  int Sq, Sk;
+  int shift;        // causal offset Sk - Sq (0 when not causal)
+  int nrb;          // 32-row query blocks per head
+  int nsplit;       // key splits per head
+  int split_tiles;  // key tiles per split
+  float c;          // scale * log2(e)
+};
+
+struct MergeParams {
+  const float* po;
+  const float* pl;
+  void* o;
+  float* lse;
+  int rows;         // B * H * Sq
+  int Sq;
+  int P;            // partials per head
+};
+
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(DecParams p) {
+  using W = FwdWave<T, D, CAUSAL, TAIL, NW, 32>;  // one 32-key block per wavefront
+  constexpr int BN = 32 * NW;                     // keys per shared tile
+  using L = FwdWave<T, D, CAUSAL, TAIL, NW, BN>;  // the tile loaders
+  constexpr int BLOCK = 32 * W::ROW_BYTES;        // one wavefront's block of a tile
+  __shared__ __attribute__((aligned(1024))) char k_lds[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds[L::TILE_BYTES];
+
+  const int split = blockIdx.x % p.nsplit;
+  const int rest = blockIdx.x / p.nsplit;
+  const int rb = rest % p.nrb;
+  const int bh = rest / p.nrb;
+
+  W w;
+  w.lane = threadIdx.x & 63;
+  w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar partial address
+  w.h = w.lane >> 5;
+  w.col = w.lane & 31;
+  w.qw = rb * 32;
+  w.myq = w.qw + w.col;
+  w.S = p.Sq;
+  w.Sk = p.Sk;
+  w.shift = p.shift;
+  w.c = p.c;
+  w.head_bytes = (uint32_t)p.Sq * W::ROW_BYTES;
+  w.kv_head_bytes = (uint32_t)p.Sk * W::ROW_BYTES;
+  const size_t kv_head_elems = (size_t)bh * p.Sk * D;
+  w.kh = (const char*)p.k + kv_head_elems * 2;
+  w.vh = (const char*)p.v + kv_head_elems * 2;
+  w.load_q((const char*)p.q + (size_t)bh * p.Sq * D * 2);
+
+  L ld;
+  ld.lane = w.lane;
+  ld.wave = w.wave;
+  ld.kh = w.kh;
+  ld.vh = w.vh;
+  ld.kv_head_bytes = w.kv_head_bytes;
+
+  // tiles [t_lo, t_hi) of this split; causal: none past the block's last row
+  const int kv_end = CAUSAL ? min(p.Sk, w.qw + 32 + p.shift) : p.Sk;
+  const int t_lo = split * p.split_tiles;
+  const int t_hi = min(kv_end > 0 ? (kv_end + BN - 1) / BN : 0, t_lo + p.split_tiles);
+
+  // One LDS stage: load a tile, wait, compute it, release it.  The compute is
+  // short next to the load, and the other work-groups on the compute unit
+  // keep HBM busy meanwhile, so a second stage would only halve the bytes in
+  // flight per work-group.
+  for (int t = t_lo; t < t_hi; ++t) {
+    ld.issue_k(t, k_lds);
+    ld.issue_v(t, v_lds);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    barrier();
+    const int k0 = t * BN + w.wave * 32;
+    if (k0 < p.Sk && w.active(k0)) {
+      w.scores(k_lds + w.wave * BLOCK);
+      w.softmax(k0);
+      w.pv(v_lds + w.wave * BLOCK);
+    }
+    barrier();
+  }
+
+  const int P = p.nsplit * NW;
+  const size_t part = ((size_t)bh * P + split * NW + w.wave) * p.Sq;
+  w.store_partial(p.po + part * D, p.pl + part);
+}
+
+// One wavefront per (head, query row): LSE = M + ln sum_p exp(LSE_p - M) with
+// M = max_p LSE_p, O = sum_p exp(LSE_p - LSE) O_p.  Lane l holds d-columns
+// l * D/64 .. +D/64.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.rows) return;
+  const int bh = row / p.Sq, i = row % p.Sq;
+  const float* pl = p.pl + (size_t)bh * p.P * p.Sq + i;
+  const float* po = p.po + ((size_t)bh * p.P * p.Sq + i) * D + lane * E;
+  const size_t ostride = (size_t)p.Sq * D;
+
+  float m = -__builtin_inff();
+  for (int q = 0; q < p.P; ++q) m = fmaxf(m, pl[(size_t)q * p.Sq]);
+  float acc[E] = {};
+  float sum = 0.f;
+  if (m != -__builtin_inff()) {
+    for (int q = 0; q < p.P; ++q) {
+      const float wq = __builtin_amdgcn_exp2f((pl[(size_t)q * p.Sq] - m) * 1.4426950408889634f);
+      sum += wq;
+      const float* src = po + q * ostride;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wq, src[e], acc[e]);
+    }
+  }
+  const bool none = !(sum > 0.f);
+  const float inv = none ? 0.f : 1.0f / sum;
+  T* out = (T*)p.o + (size_t)row * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[e] = (T)(acc[e] * inv);
+  if (lane == 0) p.lse[row] = none ? -__builtin_inff() : m + __builtin_amdgcn_logf(sum) * 0.69314718055994531f;
+}
+
+// Wavefronts per work-group; LDS per work-group is 2 * 32 * NW * D * 2 bytes
+// (K and V tiles): 64 KiB at d = 128, 32 KiB at d = 64.
+template <int D>
+struct DecodeShape {
+  static constexpr int NW = kDecodeWaves;
+};
+
+template <typename T, int D, bool CAUSAL, bool TAIL>
+hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
+  constexpr int NW = DecodeShape<D>::NW;
+  DecParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.po = (float*)a.workspace;
+  p.pl = (float*)((char*)a.workspace + plan.partial_o_bytes);
+  p.Sq = a.Sq;
+  p.Sk = a.Sk;
+  p.shift = a.causal ? a.Sk - a.Sq : 0;
+  p.nrb = plan.nrb;
+  p.nsplit = plan.nsplit;
+  p.split_tiles = plan.split_tiles;
+  p.c = a.scale * 1.4426950408889634f;
+  const long long grid = (long long)a.B * a.H * plan.nrb * plan.nsplit;
+  hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, TAIL, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
+                     p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MergeParams m;
+  m.po = p.po;
+  m.pl = p.pl;
+  m.o = a.o;
+  m.lse = a.lse;
+  m.rows = a.B * a.H * a.Sq;
+  m.Sq = a.Sq;
+  m.P = plan.partials;
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((m.rows + 3) / 4)), dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
+  const bool tail = a.Sk % 32 != 0;
+  if (a.causal)
+    return tail ? launch_decode_t<T, D, true, true>(a, plan, stream) : launch_decode_t<T, D, true, false>(a, plan, stream);
+  return tail ? launch_decode_t<T, D, false, true>(a, plan, stream) : launch_decode_t<T, D, false, false>(a, plan, stream);
+}
+
+}  // namespace detail
+
+using namespace detail;
+
+DecodePlan decode_plan(const DecodeArgs& a) {
+  DecodePlan plan{};
+  const int NW = kDecodeWaves;
+  const int BN = 32 * NW;
+  const long long heads = (long long)a.B * a.H;
+  plan.nrb = (a.Sq + 31) / 32;
+  const int tiles = (a.Sk + BN - 1) / BN;
+  // Enough work-groups for several per compute unit, but at least
+  // kMinSplitTiles tiles per split so the ring has something to overlap.
+  const long long blocks = heads * plan.nrb;
+  long long want = blocks > 0 ? (kDecodeTargetGroups + blocks - 1) / blocks : 1;
+  const long long most = tiles / kMinSplitTiles > 1 ? tiles / kMinSplitTiles : 1;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  plan.split_tiles = tiles > 0 ? (int)((tiles + want - 1) / want) : 1;
+  plan.nsplit = tiles > 0 ? (tiles + plan.split_tiles - 1) / plan.split_tiles : 1;
+  plan.partials = plan.nsplit * NW;
+  plan.partial_o_bytes = (size_t)heads * plan.partials * a.Sq * a.d * 4;
+  plan.workspace_bytes = plan.partial_o_bytes + (size_t)heads * plan.partials * a.Sq * 4;
+  plan.grid = heads * plan.nrb * plan.nsplit;
+  return plan;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
+  if (a.dtype == 1)
+    return a.d == 64 ? launch_decode_d<__bf16, 64>(a, plan, stream) : launch_decode_d<__bf16, 128>(a, plan, stream);
+  return a.d == 64 ? launch_decode_d<_Float16, 64>(a, plan, stream) : launch_decode_d<_Float16, 128>(a, plan, stream);
+}
+
+}  // namespace fa

@@ -42,270 +42,11 @@
 #include <stdint.h>
 
 #include "fa_device.h"
+#include "fa_fwd_wave.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace detail {
-
-// One wavefront's share of a work-group: 32 query rows of one (batch, head),
-// their Q fragments, running statistics and output accumulator, plus the
-// score tile / weights of the key tile in flight.  The work-group's NW
-// wavefronts share the K/V tiles (BN keys each) in LDS.
-template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
-struct FwdWave {
-  static constexpr int BM = NW * 32;
-  static constexpr int ROW_BYTES = D * 2;
-  static constexpr int KSTEPS = D / 16;    // MFMA k-steps of S^T over d
-  static constexpr int DB = D / 32;        // 32-row blocks of O^T (over d)
-  static constexpr int SB = BN / 32;       // 32-key blocks per tile
-  static constexpr int TILE_BYTES = BN * ROW_BYTES;
-  static constexpr int LOADS = TILE_BYTES / (NW * 64 * 16);  // 16-byte loads per lane per tile
-  static_assert(LOADS * NW * 64 * 16 == TILE_BYTES, "tile must split evenly over lanes");
-  static_assert(BN % 32 == 0, "BN must be a multiple of 32");
-
-  int lane, wave, h, col;
-  int qw;    // first query row of this wavefront
-  int myq;   // the query row this lane holds
-  int S;     // query rows
-  int Sk;    // key rows
-  int shift; // causal offset: key j is kept for query i iff j <= i + shift
-  int n;     // key tiles this work-group visits
-  float c;   // scale * log2(e)
-  const char* kh;
-  const char* vh;
-  uint32_t head_bytes;     // one head of q / o
-  uint32_t kv_head_bytes;  // one head of k / v
-
-  i16x8 qf[KSTEPS];
-  f32x16 oacc[DB];
-  f32x16 sacc[SB];   // scores of the tile between its MFMA step and its softmax
-  i16x8 pf[SB][2];   // its weights between the softmax and the P V MFMAs
-  float m_used;      // reference max (raw score units) the weights are taken against
-  float mc;          // c * m_used
-  float lsum;        // this lane's share of the row sum
-
-  // Does this wavefront have any unmasked key in the tile starting at k0?
-  __device__ __forceinline__ bool active(int k0) const { return !(CAUSAL && k0 > qw + 31 + shift); }
-
-  // Q rows -> VGPRs as the B operand of S^T = K Q^T (rows >= S read as 0).
-  __device__ __forceinline__ void load_q(const char* qh) {
-    const __amdgpu_buffer_rsrc_t rq = rsrc(qh, head_bytes);
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const uint32_t off = (uint32_t)myq * ROW_BYTES + (kk * 16 + h * 8) * 2;
-      qf[kk] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    }
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    m_used = -__builtin_inff();
-    mc = 0.f;
-    lsum = 0.f;
-  }
-
-  // HBM -> LDS copies of one key tile (BN rows of K, or of V), issued
-  // cooperatively by all NW wavefronts.
-  //
-  // LDS holds each tile "fragment-major": every 1 KiB block is exactly what
-  // one wave instruction later reads, so every LDS read is a linear,
-  // bank-conflict-free access at lane * 16 (or lane * 8) plus an immediate.
-  // A direct-to-LDS buffer load also fills 1 KiB in lane order, so each lane
-  // simply fetches the global 16-byte chunk that belongs at its slot:
-  //   K block (sb, kk): lane l holds K[32*sb + l%32][16*kk + 8*(l/32) .. +8],
-  //     the A operand of one S^T MFMA;
-  //   V block (sb, cc, tt, dp): two 512-byte halves for d-blocks 2dp, 2dp+1;
-  //     in half x, bytes 8*l .. 8*l+8 are the 4 elements that lane l passes
-  //     to ds_read_b64_tr_b16 for the V^T operand of d-block 2dp+x, key
-  //     chunk (sb, cc), sub-step tt (see pv()).
-  // Rows >= S read as 0 (buffer range check).
-  __device__ __forceinline__ void issue_k(int tile, char* kd) const {
-    const __amdgpu_buffer_rsrc_t rk = rsrc(kh, kv_head_bytes);
-    const uint32_t base = (uint32_t)tile * BN * ROW_BYTES;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int f = i * NW + wave;  // block (sb, kk)
-      const int ksb = f / KSTEPS, kk = f % KSTEPS;
-      const uint32_t off = base + (uint32_t)(ksb * 32 + (lane & 31)) * ROW_BYTES + (kk * 2 + (lane >> 5)) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + f * 1024), 16, off, 0, 0, 0);
-    }
-  }
-
-  __device__ __forceinline__ void issue_v(int tile, char* vd) const {
-    const __amdgpu_buffer_rsrc_t rv = rsrc(vh, kv_head_bytes);
-    const uint32_t base = (uint32_t)tile * BN * ROW_BYTES;
-    const int x = lane >> 5;         // which half (d-block parity)
-    const int lp = lane & 31;
-    const int vg = lp >> 3;          // 16-lane group of the reading lanes 2lp, 2lp+1
-    const int vrow = (vg >> 1) * 4 + ((lp & 7) >> 1);
-    const int vcol = x * 32 + (vg & 1) * 16 + (lp & 1) * 8;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int f = i * NW + wave;  // block ((sb * 2 + cc) * 2 + tt) * (DB / 2) + dp
-      const int dp = f % (DB / 2), rest = f / (DB / 2);
-      const uint32_t off = base + (uint32_t)(rest * 8 + vrow) * ROW_BYTES + (dp * 64 + vcol) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + f * 1024), 16, off, 0, 0, 0);
-    }
-  }
-
-  // S^T = K Q^T for the tile in `ks`: lane holds 16 scores of query `myq`
-  // per 32-key block (keys 8*(r/4) + 4*h + r%4 of the block, r = 0..15).
-  // The k-steps run in the outer loop so the SB accumulation chains
-  // interleave instead of waiting on one another.
-  __device__ __forceinline__ void scores(const char* ks) {
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) sacc[sb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      i16x8 kf[SB];
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) kf[sb] = *(const i16x8*)(ks + (sb * KSTEPS + kk) * 1024 + lane * 16);
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) sacc[sb] = Elem<T>::mma(kf[sb], qf[kk], sacc[sb]);
-    }
-  }
-
-  // O^T += V^T P^T for the tile in `vs` and the weights in pf.  For chunk cc
-  // of 32-key block sb, MFMA k-index h*8 + 4*tt + e stands for key
-  // 32*sb + 16*cc + 8*tt + 4*h + e, matching where the score accumulator put
-  // that key's weight.  ds_read_b64_tr_b16 gives lane j of each 16-lane group
-  // element j%4 of the 8 bytes addressed by lanes 4e + j/4 of its group
-  // (e = 0..3); the V block layout puts there
-  // V[32*sb + 16*cc + 8*tt + 4*(g/2) + e][32*db + 16*(g%2) + j] for group g,
-  // i.e. lane l receives V^T[d = 32*db + l%32][its 4 keys].
-  __device__ __forceinline__ void pv(const char* vs) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          i16x4 half[2];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int blk = ((sb * 2 + cc) * 2 + tt) * (DB / 2) + (db >> 1);
-            const char* a = vs + blk * 1024 + (db & 1) * 512 + lane * 8;
-            half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
-          }
-          const i16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = Elem<T>::mma(vf, pf[sb][cc], oacc[db]);
-        }
-      }
-    }
-  }
-
-  // Online-softmax update for the tile starting at k0 (scores in sacc):
-  // mask, row max, lazy rescale of O and l, weights P packed to T.  Only tiles
-  // that cross the causal diagonal or the sequence end are MASKED; the two
-  // variants are separate instantiations so the selects never run elsewhere.
-  __device__ __forceinline__ void softmax(int k0) {
-    if ((CAUSAL && k0 + BN - 1 > qw + shift) || (TAIL && k0 + BN > Sk))
-      softmax_impl<true>(k0);
-    else
-      softmax_impl<false>(k0);
-  }
-
-  template <bool MASKED>
-  __device__ __forceinline__ void softmax_impl(int k0) {
-    if (MASKED) {
-      // key k0 + t + 4h (t below) is kept iff t < Sk - k0 - 4h and, when
-      // causal, t <= myq + shift - k0 - 4h
-      const int base = k0 + 4 * h;
-      const int end = Sk - base;
-      const int last = myq + shift - base;
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = sb * 32 + 8 * (r >> 2) + (r & 3);
-          const bool ok = t < end && (!CAUSAL || t <= last);
-          sacc[sb][r] = ok ? sacc[sb][r] : -__builtin_inff();
-        }
-    }
-
-    // row max as a tree (independent max3 chains, then combined)
-    float mq[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sacc[0][4 * j], sacc[0][4 * j + 1]);
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        if (sb == 0 && (r & 3) == 0) continue;
-        mq[r >> 2] = fmaxf(mq[r >> 2], fmaxf(sacc[sb][r], sacc[sb][r + 1]));
-      }
-    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    mx = max_with_partner(mx);
-    const float m_new = fmaxf(m_used, mx);
-    const bool grow = (m_used == -__builtin_inff()) || (c * (m_new - m_used) > kRescaleMargin);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha =
-          (m_used == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(c * (m_used - m_new));
-      m_used = m_new;
-      mc = c * m_new;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    }
-
-    // weights; the row sum is kept in four partial sums (independent chains)
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][r], c, -mc));
-        if (MASKED) e[r] = (sacc[sb][r] == -__builtin_inff()) ? 0.f : e[r];
-        ls[r & 3] += e[r];
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        u32x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = Elem<T>::pack(e[8 * cc + 2 * i], e[8 * cc + 2 * i + 1]);
-        pf[sb][cc] = __builtin_bit_cast(i16x8, w);
-      }
-    }
-    lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  }
-
-  // Phase MFMA(k): P_{k-1} V_{k-1} (V from vp) and K_k Q^T (K from kc).
-  __device__ __forceinline__ void mfma_phase(int k, const char* kc, const char* vp) {
-    __builtin_amdgcn_s_setprio(1);
-    if (k >= 1 && active((k - 1) * BN)) pv(vp);
-    if (k < n && active(k * BN)) scores(kc);
-    __builtin_amdgcn_s_setprio(0);
-  }
-
-  // Phase SOFT(k): the softmax of tile k.
-  __device__ __forceinline__ void soft_phase(int k) {
-    if (k >= 0 && k < n && active(k * BN)) softmax(k * BN);
-  }
-
-  // O = O_acc / l and LSE = (c m + log2 l) ln 2; rows >= S are dropped by the
-  // descriptors' range checks.  A row that saw no key (causal, more query
-  // rows than keys) has l = 0: it stores O = 0 and LSE = -inf.
-  __device__ __forceinline__ void store(void* o, float* lse, size_t head_elems, int bh) const {
-    const float ltot = sum_with_partner(lsum);
-    const bool none = !(ltot > 0.f);
-    const float inv = none ? 0.f : 1.0f / ltot;
-    const __amdgpu_buffer_rsrc_t ro = rsrc((const char*)o + head_elems * 2, head_bytes);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        u32x2 w;
-        w[0] = Elem<T>::pack(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv);
-        w[1] = Elem<T>::pack(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv);
-        const int dcol = db * 32 + 8 * rg + 4 * h;
-        __builtin_amdgcn_raw_buffer_store_b64(w, ro, (uint32_t)myq * ROW_BYTES + dcol * 2, 0, 0);
-      }
-    if (h == 0) {
-      const __amdgpu_buffer_rsrc_t rl = rsrc(lse + (size_t)bh * S, (uint32_t)S * 4);
-      const float v = none ? -__builtin_inff() : (mc + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rl, (uint32_t)myq * 4, 0, 0);
-    }
-  }
-};
 
 // TAIL: Sk is not a multiple of BN, so the last key tile needs the
 // sequence-end mask.

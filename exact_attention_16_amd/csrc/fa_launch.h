@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI front end (fa_api.cpp) and the gfx950
-// kernels (fa_fwd.hip).  Not installed; callers use include/fa.h.
+// kernels (fa_fwd.hip, fa_bwd.hip, fa_decode.hip).  Not installed; callers use
+// include/fa.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,5 +50,44 @@ long long bwd_grid_size(const BwdArgs& a);
 
 // Enqueue the backward kernels (dQ and D first, then dK and dV) on `stream`.
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace fa
+
+namespace fa {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* workspace;  // partial results, DecodePlan::workspace_bytes
+  int B, H, Sq, Sk, d;
+  bool causal;
+  float scale;
+  int dtype;  // fa_dtype
+};
+
+// Wavefronts per work-group of the split-key pass (tiles of 32 keys each),
+// the work-groups it aims for, and the fewest key tiles a split may hold.
+constexpr int kDecodeWaves = 4;
+constexpr long long kDecodeTargetGroups = 1024;
+constexpr int kMinSplitTiles = 4;
+
+// How the split-key pass divides one call (a pure function of the shapes).
+struct DecodePlan {
+  int nrb;               // 32-row query blocks per head
+  int nsplit;            // key splits per head
+  int split_tiles;       // key tiles (32 * kDecodeWaves keys each) per split
+  int partials;          // partial results per head (nsplit * wavefronts)
+  size_t partial_o_bytes;
+  size_t workspace_bytes;
+  long long grid;        // work-groups of the split kernel
+};
+
+DecodePlan decode_plan(const DecodeArgs& a);
+
+// Enqueue the split kernel and the merge kernel on `stream`.
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
 }  // namespace fa

@@ -31,7 +31,8 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "SWEEP", "make_inputs", "make_inputs_kv", "default_scale", "torch_dtype"]
+__all__ = ["Workload", "WORKLOADS", "SWEEP", "DECODE", "DecodeWorkload", "make_inputs", "make_inputs_kv",
+           "default_scale", "torch_dtype"]
 
 
 @dataclass(frozen=True)
@@ -119,3 +120,34 @@ def make_inputs_kv(B: int, H: int, Sq: int, Sk: int, d: int, dtype: str, seed: i
     v = torch.randn((B, H, Sk, d), generator=g, dtype=torch.float32)
     dt = torch_dtype(dtype)
     return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous()
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Sq new queries per head over Sk cached keys (token-by-token decoding)."""
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    d: int
+    dtype: str
+    causal: bool
+    seed: int
+
+    def inputs(self):
+        return make_inputs_kv(self.B, self.H, self.Sq, self.Sk, self.d, self.dtype, self.seed)
+
+
+# Decoding workloads.  The pages contrast decoding with prompt processing but
+# give no decoding shapes; these take the benchmark grid's model widths (2048
+# = H * d) with one new token per sequence, at three batch / context mixes of
+# equal K/V size (1 GiB of bf16 K and V per call): many short contexts, a
+# typical batch, one long context.  The new token is the last position of
+# its sequence, so the end-aligned causal mask keeps every key; causal is on.
+DECODE = (
+    DecodeWorkload("decode_B64_S2048_d64", 64, 32, 1, 2048, 64, "bf16", True, 3001),
+    DecodeWorkload("decode_B16_S8192_d128", 16, 16, 1, 8192, 128, "bf16", True, 3002),
+    DecodeWorkload("decode_B1_S131072_d128", 1, 16, 1, 131072, 128, "bf16", True, 3003),
+)
+DECODE_BY_NAME = {w.name: w for w in DECODE}

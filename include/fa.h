@@ -1,8 +1,9 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (libfa.so).
  *
- * The operations are the FlashAttention-2 forward pass (fa_fwd, and
- * fa_fwd_kv for separate query and key lengths) and its gradients (fa_bwd).  What the forward pass computes is
+ * The operations are the FlashAttention-2 forward pass (fa_fwd; fa_fwd_kv
+ * for separate query and key lengths; fa_fwd_decode, the same split over the
+ * keys for a few queries) and its gradients (fa_bwd).  What the forward pass computes is
  * exact attention (FlashAttention-2 abstract, searcharxiv abstract page,
  * "Abstract": attention computed exactly, in memory linear in the sequence
  * length): for every batch b, head h and query row i
@@ -24,6 +25,8 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h> /* size_t */
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -42,7 +45,8 @@ enum {
   FA_ERR_ALIGN = -6,     /* a tensor not 16-byte aligned, or lse/delta not 4-byte */
   FA_ERR_ALIAS = -7,     /* an output overlaps an input or another output        */
   FA_ERR_TOO_LARGE = -8, /* S*d or Sk*d >= 2^30, or the grid exceeds 2^31-1      */
-  FA_ERR_HIP = -9        /* the HIP runtime rejected the launch (see below)      */
+  FA_ERR_HIP = -9,       /* the HIP runtime rejected the launch (see below)      */
+  FA_ERR_WORKSPACE = -10 /* fa_fwd_decode: workspace missing, short or unaligned */
 };
 
 /*
@@ -104,6 +108,50 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int Sq, int Sk, int d, int causal, float scale,
               int dtype, void* stream);
+
+/*
+ * fa_fwd_decode -- fa_fwd_kv for a few queries over many keys (token-by-token
+ * decoding), split over the keys.
+ *
+ * Same operation, arguments and results as fa_fwd_kv (end-aligned causal
+ * mask; rows without keys give o = 0, LSE = -inf), computed another way.
+ * The pages set decoding apart from prompt processing because its
+ * bottleneck differs (IPLEX blog "FlashAttention-2: making long-context
+ * attention run efficiently on GPUs", section "Document the implementation
+ * difference"): with Sq small there are about Sq flops per byte of K and V,
+ * so the pass is bound by HBM bandwidth and needs many more work-groups than
+ * B*H query blocks give.  fa_fwd_decode therefore splits each head's keys
+ * into disjoint ranges, computes a partial output and partial LSE per range,
+ * and merges them exactly:
+ *     LSE_i = ln sum_r exp(LSE_ir),   o_i = sum_r exp(LSE_ir - LSE_i) o_ir.
+ * Any Sq is accepted; it pays for Sq up to a few dozen rows, fa_fwd_kv for
+ * longer query blocks.  Results match fa_fwd_kv to rounding, not bitwise.
+ *
+ * Extra arguments:
+ *   workspace        device memory for the partial results, caller-owned,
+ *                    16-byte aligned, not overlapping any tensor, at least
+ *                    fa_fwd_decode_workspace_size(B, H, Sq, Sk, d) bytes.
+ *                    Its contents on entry do not matter and on return are
+ *                    unspecified; calls that share a workspace must be
+ *                    ordered on one stream.
+ *   workspace_bytes  its size in bytes.
+ * Errors: as fa_fwd_kv, plus FA_ERR_WORKSPACE (checked after the shape
+ * checks) and FA_ERR_ALIAS when the workspace overlaps a tensor.  The two
+ * kernels (split pass, then merge) are enqueued on `stream`; no memory is
+ * allocated and the results are deterministic.
+ */
+int fa_fwd_decode(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int B, int H, int Sq, int Sk, int d, int causal,
+                  float scale, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes fa_fwd_decode needs for these shapes (a pure function of
+ * its arguments: the key split is chosen from the shapes alone).  Returns 0
+ * when B*H*Sq == 0 or the arguments are invalid (d not 64/128, a negative
+ * size); then fa_fwd_decode needs no workspace or fails validation.
+ */
+size_t fa_fwd_decode_workspace_size(int B, int H, int Sq, int Sk, int d);
 
 /*
  * fa_bwd -- enqueue the gradients of the exact-attention forward pass.

@@ -29,8 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_kv", "fa_last_hip_error", "fa_status_string",
-                                   "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_workspace_size",
+                                   "fa_fwd_kv", "fa_last_hip_error", "fa_status_string", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in range(-9, 1):
+    for st in range(-10, 1):
         assert fa.fa_status_string(st)
     assert fa.fa_status_string(12345) == "unknown status"
     assert fa.fa_last_hip_error() == ""
@@ -150,3 +150,42 @@ def test_kv_empty_problem_is_a_no_op(lib):
         assert call_kv(q=0, k=0, v=0, o=0, lse=0, **dims) == 0
     assert call_kv(Sq=0, d=48) == -3
     assert call_kv(Sq=0, Sk=-2) == -2
+
+
+# fa_fwd_decode: fa_fwd_kv's checks, then the workspace
+WS = BASE + 64 * (1 << 20)
+
+
+def call_dec(ws=WS, ws_bytes=1 << 20, **kw):
+    a = dict(GOOD_KV)
+    a.update(kw)
+    return fa.fa_fwd_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Sq"], a["Sk"], a["d"],
+                            a["causal"], a["scale"], a["dtype"], ws, ws_bytes, None)
+
+
+def test_decode_workspace_size_is_a_pure_function(lib):
+    n = fa.fa_fwd_decode_workspace_size(1, 2, 64, 200, 64)
+    assert n > 0 and n == fa.fa_fwd_decode_workspace_size(1, 2, 64, 200, 64)
+    # grows with the query rows and the heads; 0 for empty or invalid shapes
+    assert fa.fa_fwd_decode_workspace_size(1, 2, 128, 200, 64) > n
+    assert fa.fa_fwd_decode_workspace_size(2, 2, 64, 200, 64) > n
+    for bad in ((0, 2, 64, 200, 64), (1, 2, 0, 200, 64), (1, 2, 64, -1, 64), (1, 2, 64, 200, 80),
+                (-1, 2, 64, 200, 64)):
+        assert fa.fa_fwd_decode_workspace_size(*bad) == 0
+    # one query over 8192 keys, d = 128: the split count keeps it small
+    assert fa.fa_fwd_decode_workspace_size(16, 16, 1, 8192, 128) < (1 << 22)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(Sk=-1), -2), (dict(d=96), -3), (dict(dtype=9), -4), (dict(scale=-1.0), -5),
+    (dict(o=O + 2), -6), (dict(o=Q), -7),
+    (dict(ws=0), -10), (dict(ws_bytes=16), -10), (dict(ws=WS + 8), -10),
+    (dict(ws=Q + 4096), -7), (dict(ws=O - 16), -7), (dict(ws=L - 4096), -7), (dict(ws=K + 1024), -7),
+])
+def test_decode_validation_errors(lib, kw, status):
+    assert call_dec(**kw) == status, fa.fa_status_string(status)
+
+
+def test_decode_empty_problem_is_a_no_op(lib):
+    for dims in (dict(B=0), dict(H=0), dict(Sq=0)):
+        assert call_dec(q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, **dims) == 0
