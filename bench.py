@@ -36,8 +36,11 @@ PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 40
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_device.h")]
+                  for f in ("fa_fwd.hip", "fa_fwd_wave.h", "fa_device.h")]
+DECODE_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
+                  for f in ("fa_decode.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_fa_fwd.md")
+DECODE_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_fa_decode.md")
 
 
 def flops(w) -> float:
@@ -52,24 +55,25 @@ def algorithmic_bytes(w) -> int:
     return 4 * n * 2 + w.B * w.H * w.S * 4
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources=None) -> str:
     """Identifies the kernel source the recorded HBM counters belong to."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in sources or KERNEL_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, record: str = TRAFFIC_RECORD, sources=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when the kernel source changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_RECORD):
+    if not os.path.exists(record):
         return None
-    for line in open(TRAFFIC_RECORD):
+    sha = kernel_hash(sources)
+    for line in open(record):
         if line.startswith("traffic-record:"):
             rec = json.loads(line.split(":", 1)[1])
-            if rec.get("workload") == workload and rec.get("kernel_sha") == kernel_hash():
+            if rec.get("workload") == workload and rec.get("kernel_sha") == sha:
                 return rec.get("bytes_per_launch")
     return None
 
@@ -232,6 +236,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the S x d x causal grid")
     ap.add_argument("--no-backward", action="store_true", help="skip the gradient timings")
     ap.add_argument("--no-decode", action="store_true", help="skip the split-key decoding timings")
+    ap.add_argument("--decode", default="", help="comma-separated decoding workloads (default: all)")
     ap.add_argument("--cpu-heads", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -314,7 +319,10 @@ def main():
     # bound by HBM: reported against the 8 TB/s peak.
     decode = []
     if not args.no_decode:
+        names = [n for n in args.decode.split(",") if n]
         for wd in DECODE:
+            if names and wd.name not in names:
+                continue
             steps = max(10, args.steps)
             rd = time_decode(wd, steps, args.warmup)
             msd = rd["total_ms"] / steps
@@ -322,7 +330,8 @@ def main():
             decode.append({"workload": wd.name, "B": wd.B, "H": wd.H, "Sq": wd.Sq, "Sk": wd.Sk, "d": wd.d,
                            "causal": wd.causal, "ms": msd, "algorithmic_bytes": decode_bytes(wd),
                            "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "steps": steps,
-                           "workspace_bytes": rd["workspace_bytes"], "finite": rd["finite"]})
+                           "workspace_bytes": rd["workspace_bytes"], "finite": rd["finite"],
+                           "traffic": recorded_traffic(wd.name, DECODE_TRAFFIC_RECORD, DECODE_SOURCES)})
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -12,12 +12,13 @@
 // FlashAttention-2 "sequence parallelism" applied to the other sequence axis:
 //
 // * decode_kernel: work-group = (head, 32-row query block, key split).  Its
-//   NW wavefronts load shared tiles of 32*NW keys HBM -> LDS with
-//   buffer_load ... lds; wavefront w takes 32-key block w of each tile and
-//   keeps its own online softmax over the keys it saw (the same MFMA score /
-//   output products and softmax as the prefill kernel).  Each
-//   wavefront writes its normalised partial output and partial LSE (fp32) to
-//   a caller-provided workspace: no atomics, no reduction through LDS.
+//   NW wavefronts load shared tiles of 32*NW*BPW keys HBM -> LDS with
+//   buffer_load ... lds; wavefront w takes the 32-key blocks w*BPW .. of each
+//   tile and keeps its own online softmax over the keys it saw (the same MFMA
+//   score / output products and softmax as the prefill kernel).  At the end the
+//   wavefronts' results are merged through LDS and the work-group writes one
+//   normalised partial output and partial LSE (fp32) per query row to a
+//   caller-provided workspace: no atomics.
 // * merge_kernel: one wavefront per (head, query row) combines the P
 //   partials exactly: LSE = ln sum_p exp(LSE_p) and O = sum_p exp(LSE_p - LSE)
 //   O_p.  Partials of key subsets a row cannot see have LSE_p = -inf and drop
@@ -61,10 +62,23 @@ struct MergeParams {
   int P;            // partials per head
 };
 
-template <typename T, int D, bool CAUSAL, bool TAIL, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecParams p) {
-  using W = FwdWave<T, D, CAUSAL, TAIL, NW, 32>;  // one 32-key block per wavefront
-  constexpr int BN = 32 * NW;                     // keys per shared tile
+// Work-groups per compute unit that LDS allows (K and V tiles of
+// 32 * NW * BPW keys, 160 KiB per compute unit); the register budget is set to match, at most 4
+// wavefronts per SIMD (128 registers), or 3 for the masked d = 64 variants,
+// which need about 132.
+template <int D, int NW, int BPW>
+constexpr int decode_groups_per_cu() { return (160 * 1024) / (2 * 32 * NW * BPW * D * 2); }
+template <int D, int NW, int BPW, bool MASKS>
+constexpr int decode_waves_per_simd() {
+  return decode_groups_per_cu<D, NW, BPW>() * NW / 4 < (MASKS ? 3 : 8) ? decode_groups_per_cu<D, NW, BPW>() * NW / 4
+                                                                       : (MASKS ? 3 : 8);
+}
+
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BPW>
+__global__ __launch_bounds__(NW * 64, (decode_waves_per_simd<D, NW, BPW, CAUSAL || TAIL>())) void decode_kernel(
+    DecParams p) {
+  using W = FwdWave<T, D, CAUSAL, TAIL, 1, 32>;  // one 32-key block per wavefront (its own loaders unused)
+  constexpr int BN = 32 * NW * BPW;               // keys per shared tile
   using L = FwdWave<T, D, CAUSAL, TAIL, NW, BN>;  // the tile loaders
   constexpr int BLOCK = 32 * W::ROW_BYTES;        // one wavefront's block of a tile
   __shared__ __attribute__((aligned(1024))) char k_lds[L::TILE_BYTES];
@@ -114,18 +128,100 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecParams p) {
     ld.issue_v(t, v_lds);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     barrier();
-    const int k0 = t * BN + w.wave * 32;
-    if (k0 < p.Sk && w.active(k0)) {
-      w.scores(k_lds + w.wave * BLOCK);
-      w.softmax(k0);
-      w.pv(v_lds + w.wave * BLOCK);
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+      const int blk = w.wave * BPW + b;  // this wavefront's blocks are adjacent
+      const int k0 = t * BN + blk * 32;
+      if (k0 < p.Sk && w.active(k0)) {
+        w.scores(k_lds + blk * BLOCK);
+        w.softmax(k0);
+        w.pv(v_lds + blk * BLOCK);
+      }
     }
     barrier();
   }
 
-  const int P = p.nsplit * NW;
-  const size_t part = ((size_t)bh * P + split * NW + w.wave) * p.Sq;
-  w.store_partial(p.po + part * D, p.pl + part);
+  // Combine the NW wavefronts' results in log2(NW) rounds through LDS (the
+  // tiles are free now).  Each wavefront first normalises its own: O_w =
+  // O_acc / l_w and LSE_w per row.  In a round with `half` active pairs,
+  // wavefront w + half stages O_w and LSE_w lane-major (every lane writes and
+  // its partner lane reads the same 16-byte slots, so no bank conflicts) and
+  // wavefront w merges them into its registers:
+  //   M = max(LSE_a, LSE_b), LSE = M + ln(e^(LSE_a - M) + e^(LSE_b - M)),
+  //   O = (e^(LSE_a - M) O_a + e^(LSE_b - M) O_b) / (e^(LSE_a - M) + e^(LSE_b - M)).
+  // Wavefront 0 ends with the work-group's result and writes it as this
+  // split's partial.
+  constexpr int DB = W::DB;
+  static_assert((NW / 2) * 64 * DB * 16 * 4 <= L::TILE_BYTES, "staging fits a tile buffer");
+  float lse_w;
+  {
+    const float ltot = sum_with_partner(w.lsum);
+    const bool none = !(ltot > 0.f);
+    const float inv = none ? 0.f : 1.0f / ltot;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) w.oacc[db] *= inv;
+    lse_w = none ? -__builtin_inff() : (w.mc + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f;
+  }
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half /= 2) {
+    barrier();
+    if (w.wave >= half && w.wave < 2 * half) {
+      f32x4* so = (f32x4*)k_lds + (w.wave - half) * 64 * DB * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = w.oacc[db][4 * rg + e];
+          so[(db * 4 + rg) * 64 + w.lane] = x;
+        }
+      ((float*)v_lds)[(w.wave - half) * 64 + w.lane] = lse_w;
+    }
+    barrier();
+    if (w.wave < half) {
+      const f32x4* so = (const f32x4*)k_lds + w.wave * 64 * DB * 4;
+      const float lse_p = ((const float*)v_lds)[w.wave * 64 + w.lane];
+      const float m = fmaxf(lse_w, lse_p);
+      const bool none = m == -__builtin_inff();
+      const float a = none ? 0.f : __builtin_amdgcn_exp2f((lse_w - m) * 1.4426950408889634f);
+      const float b = none ? 0.f : __builtin_amdgcn_exp2f((lse_p - m) * 1.4426950408889634f);
+      const float inv = none ? 0.f : 1.0f / (a + b);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 x = so[(db * 4 + rg) * 64 + w.lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w.oacc[db][4 * rg + e] = (a * w.oacc[db][4 * rg + e] + b * x[e]) * inv;
+        }
+      lse_w = none ? -__builtin_inff() : m + __builtin_amdgcn_logf(a + b) * 0.69314718055994531f;
+    }
+  }
+  if (w.wave == 0) {
+    // this split's partial: rows [qw, qw + 32) of [Sq][D] (rows >= Sq dropped
+    // by the range checks)
+    const size_t part = ((size_t)bh * p.nsplit + split) * p.Sq;
+    const __amdgpu_buffer_rsrc_t ro = rsrc(p.po + part * D, (uint32_t)p.Sq * D * 4);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        // (a whole-vector bit_cast: bit_cast of a single vector element
+        // miscompiles to element 0 with this toolchain)
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = w.oacc[db][4 * rg + e];
+        const int dcol = db * 32 + 8 * rg + 4 * w.h;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), ro, ((uint32_t)w.myq * D + dcol) * 4, 0,
+                                               0);
+      }
+    if (w.h == 0) {
+      const __amdgpu_buffer_rsrc_t rl = rsrc(p.pl + part, (uint32_t)p.Sq * 4);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, lse_w), rl, (uint32_t)w.myq * 4, 0, 0);
+    }
+  }
 }
 
 // One wavefront per (head, query row): LSE = M + ln sum_p exp(LSE_p - M) with
@@ -143,10 +239,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const size_t ostride = (size_t)p.Sq * D;
 
   float m = -__builtin_inff();
+#pragma unroll 8
   for (int q = 0; q < p.P; ++q) m = fmaxf(m, pl[(size_t)q * p.Sq]);
   float acc[E] = {};
   float sum = 0.f;
   if (m != -__builtin_inff()) {
+#pragma unroll 8
     for (int q = 0; q < p.P; ++q) {
       const float wq = __builtin_amdgcn_exp2f((pl[(size_t)q * p.Sq] - m) * 1.4426950408889634f);
       sum += wq;
@@ -163,16 +261,17 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (lane == 0) p.lse[row] = none ? -__builtin_inff() : m + __builtin_amdgcn_logf(sum) * 0.69314718055994531f;
 }
 
-// Wavefronts per work-group; LDS per work-group is 2 * 32 * NW * D * 2 bytes
-// (K and V tiles): 64 KiB at d = 128, 32 KiB at d = 64.
+// Wavefronts and blocks per wavefront; LDS per work-group is
+// 2 * 32 * NW * BPW * D * 2 bytes (K and V tiles).
 template <int D>
 struct DecodeShape {
-  static constexpr int NW = kDecodeWaves;
+  static constexpr int NW = decode_waves(D);
+  static constexpr int BPW = decode_blocks_per_wave(D);
 };
 
 template <typename T, int D, bool CAUSAL, bool TAIL>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
-  constexpr int NW = DecodeShape<D>::NW;
+  constexpr int NW = DecodeShape<D>::NW, BPW = DecodeShape<D>::BPW;
   DecParams p;
   p.q = a.q;
   p.k = a.k;
@@ -187,7 +286,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStrea
   p.split_tiles = plan.split_tiles;
   p.c = a.scale * 1.4426950408889634f;
   const long long grid = (long long)a.B * a.H * plan.nrb * plan.nsplit;
-  hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, TAIL, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, TAIL, NW, BPW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
                      p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -206,7 +305,9 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStrea
 template <typename T, int D>
 hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
   const bool tail = a.Sk % 32 != 0;
-  if (a.causal)
+  // End-aligned, the causal mask keeps every key of a single query row, so
+  // Sq = 1 (the usual decoding step) runs the unmasked kernel.
+  if (a.causal && a.Sq > 1)
     return tail ? launch_decode_t<T, D, true, true>(a, plan, stream) : launch_decode_t<T, D, true, false>(a, plan, stream);
   return tail ? launch_decode_t<T, D, false, true>(a, plan, stream) : launch_decode_t<T, D, false, false>(a, plan, stream);
 }
@@ -217,8 +318,7 @@ using namespace detail;
 
 DecodePlan decode_plan(const DecodeArgs& a) {
   DecodePlan plan{};
-  const int NW = kDecodeWaves;
-  const int BN = 32 * NW;
+  const int BN = decode_tile_keys(a.d);
   const long long heads = (long long)a.B * a.H;
   plan.nrb = (a.Sq + 31) / 32;
   const int tiles = (a.Sk + BN - 1) / BN;
@@ -231,7 +331,7 @@ DecodePlan decode_plan(const DecodeArgs& a) {
   if (want < 1) want = 1;
   plan.split_tiles = tiles > 0 ? (int)((tiles + want - 1) / want) : 1;
   plan.nsplit = tiles > 0 ? (tiles + plan.split_tiles - 1) / plan.split_tiles : 1;
-  plan.partials = plan.nsplit * NW;
+  plan.partials = plan.nsplit;
   plan.partial_o_bytes = (size_t)heads * plan.partials * a.Sq * a.d * 4;
   plan.workspace_bytes = plan.partial_o_bytes + (size_t)heads * plan.partials * a.Sq * 4;
   plan.grid = heads * plan.nrb * plan.nsplit;

@@ -246,32 +246,6 @@ struct FwdWave {
     if (k >= 0 && k < n && active(k * BN)) softmax(k * BN);
   }
 
-  // The same normalisation into fp32 partial results (the split-key decode):
-  // po [S][D] and pl [S] of this wavefront's key subset; a row that saw no
-  // key of the subset stores O = 0 and LSE = -inf, so it drops out of the
-  // merge.  Rows >= S are dropped by the descriptors' range checks.
-  __device__ __forceinline__ void store_partial(float* po, float* pl) const {
-    const float ltot = sum_with_partner(lsum);
-    const bool none = !(ltot > 0.f);
-    const float inv = none ? 0.f : 1.0f / ltot;
-    const __amdgpu_buffer_rsrc_t ro = rsrc(po, (uint32_t)S * D * 4);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = __builtin_bit_cast(unsigned, oacc[db][4 * rg + e] * inv);
-        const int dcol = db * 32 + 8 * rg + 4 * h;
-        __builtin_amdgcn_raw_buffer_store_b128(w, ro, ((uint32_t)myq * D + dcol) * 4, 0, 0);
-      }
-    if (h == 0) {
-      const __amdgpu_buffer_rsrc_t rl = rsrc(pl, (uint32_t)S * 4);
-      const float v = none ? -__builtin_inff() : (mc + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rl, (uint32_t)myq * 4, 0, 0);
-    }
-  }
-
   // O = O_acc / l and LSE = (c m + log2 l) ln 2; rows >= S are dropped by the
   // descriptors' range checks.  A row that saw no key (causal, more query
   // rows than keys) has l = 0: it stores O = 0 and LSE = -inf.

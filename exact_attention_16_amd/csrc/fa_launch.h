@@ -68,18 +68,25 @@ struct DecodeArgs {
   int dtype;  // fa_dtype
 };
 
-// Wavefronts per work-group of the split-key pass (tiles of 32 keys each),
-// the work-groups it aims for, and the fewest key tiles a split may hold.
-constexpr int kDecodeWaves = 4;
-constexpr long long kDecodeTargetGroups = 1024;
+// Shape of the split-key pass for head dimension d: wavefronts per
+// work-group, 32-key blocks per wavefront in each shared key tile, the
+// work-groups it aims for, and the fewest key tiles a split may hold.  Chosen
+// by measurement on the MI355X (1 GiB K/V caches): tiles of 128 keys at
+// d = 64 and 64 keys at d = 128 (32 KiB of K and V per work-group), and about
+// two work-groups per compute unit, read the caches fastest; more resident
+// work-groups (more concurrent streams) read them more slowly.
+constexpr int decode_waves(int d) { return d == 64 ? 2 : 2; }
+constexpr int decode_blocks_per_wave(int d) { return d == 64 ? 2 : 1; }
+constexpr int decode_tile_keys(int d) { return 32 * decode_waves(d) * decode_blocks_per_wave(d); }
+constexpr long long kDecodeTargetGroups = 512;
 constexpr int kMinSplitTiles = 4;
 
 // How the split-key pass divides one call (a pure function of the shapes).
 struct DecodePlan {
   int nrb;               // 32-row query blocks per head
   int nsplit;            // key splits per head
-  int split_tiles;       // key tiles (32 * kDecodeWaves keys each) per split
-  int partials;          // partial results per head (nsplit * wavefronts)
+  int split_tiles;       // key tiles (decode_tile_keys(d) keys each) per split
+  int partials;          // partial results per head and query row (= nsplit)
   size_t partial_o_bytes;
   size_t workspace_bytes;
   long long grid;        // work-groups of the split kernel
