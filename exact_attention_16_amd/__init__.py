@@ -11,6 +11,7 @@ loaded on first use and its absence is an error.
 from .binding import (  # noqa: F401
     FA_DTYPE_BF16,
     FA_DTYPE_FP16,
+    FA_ERR_STRIDE,
     FA_ERR_WORKSPACE,
     FaError,
     backward,
@@ -18,8 +19,10 @@ from .binding import (  # noqa: F401
     fa_bwd,
     fa_fwd,
     fa_fwd_decode,
+    fa_fwd_decode_strided,
     fa_fwd_decode_workspace_size,
     fa_fwd_kv,
+    fa_fwd_strided,
     fa_last_hip_error,
     fa_status_string,
     fa_version,

@@ -20,6 +20,7 @@ FA_DTYPE_BF16 = 1
 FA_OK = 0
 FA_ERR_HIP = -9
 FA_ERR_WORKSPACE = -10
+FA_ERR_STRIDE = -11
 
 _DTYPES = {torch.float16: FA_DTYPE_FP16, torch.bfloat16: FA_DTYPE_BF16}
 
@@ -49,6 +50,11 @@ def load_library() -> ctypes.CDLL:
             lib.fa_fwd_kv.restype = i
             lib.fa_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
             lib.fa_fwd_decode.restype = i
+            lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp]
+            lib.fa_fwd_strided.restype = i
+            lib.fa_fwd_decode_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp,
+                                                  ctypes.c_size_t, vp]
+            lib.fa_fwd_decode_strided.restype = i
             lib.fa_fwd_decode_workspace_size.argtypes = [i, i, i, i, i]
             lib.fa_fwd_decode_workspace_size.restype = ctypes.c_size_t
             lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
@@ -94,6 +100,31 @@ def fa_fwd_decode(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, worksp
                                              float(scale), int(dtype), workspace, int(workspace_bytes), stream))
 
 
+def _strides_arg(strides):
+    """12 element strides as a host int64 array (None stays NULL)."""
+    if strides is None:
+        return None
+    arr = (ctypes.c_longlong * 12)(*[int(x) for x in strides])
+    return ctypes.cast(arr, ctypes.c_void_p), arr  # keep arr alive with the pointer
+
+
+def fa_fwd_strided(q, k, v, o, lse, B, H, Sq, Sk, d, strides, causal, scale, dtype, stream) -> int:
+    """The C entry point; ``strides`` is a sequence of 12 element strides (q, k,
+    v, o: batch, head, row) or None; returns the status."""
+    arg = _strides_arg(strides)
+    return int(load_library().fa_fwd_strided(q, k, v, o, lse, int(B), int(H), int(Sq), int(Sk), int(d),
+                                              arg[0] if arg else None, int(causal), float(scale), int(dtype),
+                                              stream))
+
+
+def fa_fwd_decode_strided(q, k, v, o, lse, B, H, Sq, Sk, d, strides, causal, scale, dtype, workspace,
+                          workspace_bytes, stream) -> int:
+    arg = _strides_arg(strides)
+    return int(load_library().fa_fwd_decode_strided(q, k, v, o, lse, int(B), int(H), int(Sq), int(Sk), int(d),
+                                                     arg[0] if arg else None, int(causal), float(scale),
+                                                     int(dtype), workspace, int(workspace_bytes), stream))
+
+
 def fa_fwd_decode_workspace_size(B, H, Sq, Sk, d) -> int:
     return int(load_library().fa_fwd_decode_workspace_size(int(B), int(H), int(Sq), int(Sk), int(d)))
 
@@ -113,6 +144,24 @@ class FaError(RuntimeError):
         self.status = status
 
 
+def _layout(q, k, v, o):
+    """None when q, k, v and o are all contiguous; else their 12 element
+    strides (batch, head, row each) for the strided entry points, which need
+    the head dimension contiguous."""
+    ts = (q, k, v, o)
+    if all(t.is_contiguous() for t in ts):
+        return None
+    if any(t.dim() != 4 or (t.shape[3] > 1 and t.stride(3) != 1) for t in ts):
+        raise ValueError("q, k, v and out need a contiguous last (head) dimension")
+    out = []
+    for t in ts:
+        # a size-1 dimension's stride is arbitrary in torch: batch / head get
+        # 0, a single row gets d (rows past the end must stay out of range)
+        out += [t.stride(0) if t.shape[0] > 1 else 0, t.stride(1) if t.shape[1] > 1 else 0,
+                t.stride(2) if t.shape[2] > 1 else t.shape[3]]
+    return out
+
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             scale: float | None = None, out: torch.Tensor | None = None,
             lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
@@ -121,8 +170,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
 
     Returns (o [B, H, Sq, d] in the input dtype, lse [B, H, Sq] float32).
     With Sq != Sk this is fa_fwd_kv (causal mask aligned to the sequence
-    end), else fa_fwd.  The launch is asynchronous on ``stream`` (default:
-    the current stream).
+    end), else fa_fwd; tensors that are not contiguous (e.g. [B, S, H, d]
+    storage viewed as [B, H, S, d], or a slice of a cache) go to
+    fa_fwd_strided, and a default ``out`` takes q's layout.  The launch is
+    asynchronous on ``stream`` (default: the current stream).
     """
     if (q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[:2] != q.shape[:2]
             or k.shape[3] != q.shape[3]):
@@ -132,8 +183,6 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         raise TypeError("q, k, v must all be float16 or all bfloat16")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
     B, H, S, d = q.shape
     Sk = k.shape[2]
     if scale is None:
@@ -142,12 +191,17 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be a tensor like q")
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    if Sk == S:
+    strides = _layout(q, k, v, out)
+    if strides is not None:
+        st, entry = fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   B, H, S, Sk, d, strides, 1 if causal else 0, scale, _DTYPES[q.dtype],
+                                   s.cuda_stream), "fa_fwd_strided"
+    elif Sk == S:
         st, entry = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                            B, H, S, d, 1 if causal else 0, scale, _DTYPES[q.dtype], s.cuda_stream), "fa_fwd"
     else:
@@ -167,7 +221,9 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
 
     ``workspace`` is a uint8 device tensor of at least
     ``fa_fwd_decode_workspace_size(B, H, Sq, Sk, d)`` bytes (allocated here if
-    not given).  Returns (o, lse).  Asynchronous on ``stream``.
+    not given).  Non-contiguous tensors (e.g. the first Sk rows of a
+    [B, S_max, H, d] cache viewed as [B, H, Sk, d]) go to
+    fa_fwd_decode_strided.  Returns (o, lse).  Asynchronous on ``stream``.
     """
     if (q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[:2] != q.shape[:2]
             or k.shape[3] != q.shape[3]):
@@ -175,16 +231,16 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
                          f"{tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
         raise TypeError("q, k, v must all be float16 or all bfloat16")
-    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v)):
-        raise ValueError("q, k, v must be contiguous device tensors")
+    if not all(t.is_cuda for t in (q, k, v)):
+        raise ValueError("q, k, v must be device tensors")
     B, H, Sq, d = q.shape
     Sk = k.shape[2]
     if scale is None:
         scale = float(torch.tensor(d, dtype=torch.float32).rsqrt())
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be a tensor like q")
     if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
     need = fa_fwd_decode_workspace_size(B, H, Sq, Sk, d)
@@ -194,10 +250,18 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    st = fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Sq, Sk, d,
-                       1 if causal else 0, scale, _DTYPES[q.dtype], workspace.data_ptr(), nbytes, s.cuda_stream)
+    strides = _layout(q, k, v, out)
+    if strides is None:
+        st, entry = fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                  Sq, Sk, d, 1 if causal else 0, scale, _DTYPES[q.dtype], workspace.data_ptr(),
+                                  nbytes, s.cuda_stream), "fa_fwd_decode"
+    else:
+        st, entry = fa_fwd_decode_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                          lse.data_ptr(), B, H, Sq, Sk, d, strides, 1 if causal else 0, scale,
+                                          _DTYPES[q.dtype], workspace.data_ptr(), nbytes,
+                                          s.cuda_stream), "fa_fwd_decode_strided"
     if st != FA_OK:
-        raise FaError(st, "fa_fwd_decode")
+        raise FaError(st, entry)
     return out, lse
 
 

@@ -50,6 +50,11 @@ struct DecParams {
   int nsplit;       // key splits per head
   int split_tiles;  // key tiles per split
   float c;          // scale * log2(e)
+  // strided layouts only: heads per batch entry, batch / head strides
+  // (elements) and row strides (bytes) of q, k, v
+  int H;
+  long long qsb, qsh, ksb, ksh, vsb, vsh;
+  uint32_t q_rs, k_rs, v_rs;
 };
 
 struct MergeParams {
@@ -60,10 +65,13 @@ struct MergeParams {
   int rows;         // B * H * Sq
   int Sq;
   int P;            // partials per head
+  int H;
+  long long osb, osh, osr;  // element strides of o: batch, head, row
 };
 
 // Work-groups per compute unit that LDS allows (K and V tiles of
-// 32 * NW * BPW keys, 160 KiB per compute unit); the register budget is set to match, at most 4
+// 32 * NW * BPW keys, 160 KiB per compute unit); the register budget is set
+// to match, at most 4
 // wavefronts per SIMD (128 registers), or 3 for the masked d = 64 variants,
 // which need about 132.
 template <int D, int NW, int BPW>
@@ -74,12 +82,13 @@ constexpr int decode_waves_per_simd() {
                                                                        : (MASKS ? 3 : 8);
 }
 
-template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BPW>
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BPW, bool STRIDED>
 __global__ __launch_bounds__(NW * 64, (decode_waves_per_simd<D, NW, BPW, CAUSAL || TAIL>())) void decode_kernel(
     DecParams p) {
-  using W = FwdWave<T, D, CAUSAL, TAIL, 1, 32>;  // one 32-key block per wavefront (its own loaders unused)
-  constexpr int BN = 32 * NW * BPW;               // keys per shared tile
-  using L = FwdWave<T, D, CAUSAL, TAIL, NW, BN>;  // the tile loaders
+  // one 32-key block per wavefront (its own loaders unused)
+  using W = FwdWave<T, D, CAUSAL, TAIL, 1, 32, STRIDED>;
+  constexpr int BN = 32 * NW * BPW;                        // keys per shared tile
+  using L = FwdWave<T, D, CAUSAL, TAIL, NW, BN, STRIDED>;  // the tile loaders
   constexpr int BLOCK = 32 * W::ROW_BYTES;        // one wavefront's block of a tile
   __shared__ __attribute__((aligned(1024))) char k_lds[L::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds[L::TILE_BYTES];
@@ -100,19 +109,28 @@ __global__ __launch_bounds__(NW * 64, (decode_waves_per_simd<D, NW, BPW, CAUSAL 
   w.Sk = p.Sk;
   w.shift = p.shift;
   w.c = p.c;
-  w.head_bytes = (uint32_t)p.Sq * W::ROW_BYTES;
-  w.kv_head_bytes = (uint32_t)p.Sk * W::ROW_BYTES;
-  const size_t kv_head_elems = (size_t)bh * p.Sk * D;
-  w.kh = (const char*)p.k + kv_head_elems * 2;
-  w.vh = (const char*)p.v + kv_head_elems * 2;
-  w.load_q((const char*)p.q + (size_t)bh * p.Sq * D * 2);
-
   L ld;
+  if constexpr (STRIDED) {
+    const int b = bh / p.H, hh = bh - b * p.H;
+    w.q_rs = p.q_rs;
+    w.head_bytes = (uint32_t)(p.Sq - 1) * p.q_rs + W::ROW_BYTES;
+    ld.k_rs = p.k_rs;
+    ld.v_rs = p.v_rs;
+    ld.kv_head_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * p.k_rs + W::ROW_BYTES : 0u;
+    ld.v_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * p.v_rs + W::ROW_BYTES : 0u;
+    ld.kh = (const char*)p.k + (b * p.ksb + hh * p.ksh) * 2;
+    ld.vh = (const char*)p.v + (b * p.vsb + hh * p.vsh) * 2;
+    w.load_q((const char*)p.q + (b * p.qsb + hh * p.qsh) * 2);
+  } else {
+    w.head_bytes = (uint32_t)p.Sq * W::ROW_BYTES;
+    ld.kv_head_bytes = (uint32_t)p.Sk * W::ROW_BYTES;
+    const size_t kv_head_elems = (size_t)bh * p.Sk * D;
+    ld.kh = (const char*)p.k + kv_head_elems * 2;
+    ld.vh = (const char*)p.v + kv_head_elems * 2;
+    w.load_q((const char*)p.q + (size_t)bh * p.Sq * D * 2);
+  }
   ld.lane = w.lane;
   ld.wave = w.wave;
-  ld.kh = w.kh;
-  ld.vh = w.vh;
-  ld.kv_head_bytes = w.kv_head_bytes;
 
   // tiles [t_lo, t_hi) of this split; causal: none past the block's last row
   const int kv_end = CAUSAL ? min(p.Sk, w.qw + 32 + p.shift) : p.Sk;
@@ -255,7 +273,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   }
   const bool none = !(sum > 0.f);
   const float inv = none ? 0.f : 1.0f / sum;
-  T* out = (T*)p.o + (size_t)row * D + lane * E;
+  const int b = bh / p.H, hh = bh - b * p.H;
+  T* out = (T*)p.o + b * p.osb + hh * p.osh + i * p.osr + lane * E;
 #pragma unroll
   for (int e = 0; e < E; ++e) out[e] = (T)(acc[e] * inv);
   if (lane == 0) p.lse[row] = none ? -__builtin_inff() : m + __builtin_amdgcn_logf(sum) * 0.69314718055994531f;
@@ -269,7 +288,7 @@ struct DecodeShape {
   static constexpr int BPW = decode_blocks_per_wave(D);
 };
 
-template <typename T, int D, bool CAUSAL, bool TAIL>
+template <typename T, int D, bool CAUSAL, bool TAIL, bool STRIDED>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
   constexpr int NW = DecodeShape<D>::NW, BPW = DecodeShape<D>::BPW;
   DecParams p;
@@ -285,9 +304,19 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStrea
   p.nsplit = plan.nsplit;
   p.split_tiles = plan.split_tiles;
   p.c = a.scale * 1.4426950408889634f;
+  p.H = a.H;
+  // o's element strides (batch, head, row), for the merge
+  long long osb = (long long)a.H * a.Sq * D, osh = (long long)a.Sq * D, osr = D;
+  if (STRIDED) {
+    const long long* st = a.strides;  // q, k, v, o: batch, head, row (elements)
+    p.qsb = st[0]; p.qsh = st[1]; p.q_rs = (uint32_t)(st[2] * 2);
+    p.ksb = st[3]; p.ksh = st[4]; p.k_rs = (uint32_t)(st[5] * 2);
+    p.vsb = st[6]; p.vsh = st[7]; p.v_rs = (uint32_t)(st[8] * 2);
+    osb = st[9]; osh = st[10]; osr = st[11];
+  }
   const long long grid = (long long)a.B * a.H * plan.nrb * plan.nsplit;
-  hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, TAIL, NW, BPW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
-                     p);
+  hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, TAIL, NW, BPW, STRIDED>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeParams m;
@@ -298,18 +327,29 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStrea
   m.rows = a.B * a.H * a.Sq;
   m.Sq = a.Sq;
   m.P = plan.partials;
+  m.H = a.H;
+  m.osb = osb;
+  m.osh = osh;
+  m.osr = osr;
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((m.rows + 3) / 4)), dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
+template <typename T, int D, bool STRIDED>
+hipError_t launch_decode_s(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
   const bool tail = a.Sk % 32 != 0;
   // End-aligned, the causal mask keeps every key of a single query row, so
   // Sq = 1 (the usual decoding step) runs the unmasked kernel.
   if (a.causal && a.Sq > 1)
-    return tail ? launch_decode_t<T, D, true, true>(a, plan, stream) : launch_decode_t<T, D, true, false>(a, plan, stream);
-  return tail ? launch_decode_t<T, D, false, true>(a, plan, stream) : launch_decode_t<T, D, false, false>(a, plan, stream);
+    return tail ? launch_decode_t<T, D, true, true, STRIDED>(a, plan, stream)
+                : launch_decode_t<T, D, true, false, STRIDED>(a, plan, stream);
+  return tail ? launch_decode_t<T, D, false, true, STRIDED>(a, plan, stream)
+              : launch_decode_t<T, D, false, false, STRIDED>(a, plan, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
+  return a.strides ? launch_decode_s<T, D, true>(a, plan, stream) : launch_decode_s<T, D, false>(a, plan, stream);
 }
 
 }  // namespace detail

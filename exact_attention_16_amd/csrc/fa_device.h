@@ -69,6 +69,11 @@ struct Params {
   int shift;   // causal offset: query row i sits at key position i + shift (Sk - S)
   int nqb;     // query-row blocks per head
   float c;     // scale * log2(e): scores enter exp2 as c * s
+  // Strided layouts only: heads per batch entry, the batch and head strides
+  // (elements) of q, k, v, o, and their row strides (bytes).
+  int H;
+  long long qsb, qsh, ksb, ksh, vsb, vsh, osb, osh;
+  uint32_t q_rs, k_rs, v_rs, o_rs;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {

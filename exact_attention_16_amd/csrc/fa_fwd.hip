@@ -76,10 +76,10 @@ namespace detail {
 template <int D, bool CAUSAL, bool TAIL>
 constexpr int waves_per_simd() { return (D == 64 && (CAUSAL || !TAIL)) ? 4 : 2; }
 
-template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN, bool STRIDED>
 __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void fwd_kernel(Params p) {
   static_assert(NW == 8, "the ping-pong schedule pairs wavefronts w and w+4 on one SIMD");
-  using W = FwdWave<T, D, CAUSAL, TAIL, NW, BN>;
+  using W = FwdWave<T, D, CAUSAL, TAIL, NW, BN, STRIDED>;
   // K and V double buffers as four distinct LDS objects; the step loop is
   // unrolled by two so each access names its buffer at compile time, which
   // lets the compiler see that reads of one buffer never alias the
@@ -134,12 +134,30 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
   w.c = p.c;
 
   const size_t head_elems = (size_t)bh * p.S * D;
-  const size_t kv_head_elems = (size_t)bh * p.Sk * D;
-  w.head_bytes = (uint32_t)p.S * W::ROW_BYTES;
-  w.kv_head_bytes = (uint32_t)p.Sk * W::ROW_BYTES;
-  w.kh = (const char*)p.k + kv_head_elems * 2;
-  w.vh = (const char*)p.v + kv_head_elems * 2;
-  w.load_q((const char*)p.q + head_elems * 2);
+  if constexpr (STRIDED) {
+    // head bases from the batch and head strides; each range ends with the
+    // head's last row, so rows past S (or Sk) read as 0 / are dropped
+    const int b = bh / p.H, hh = bh - b * p.H;
+    w.q_rs = p.q_rs;
+    w.k_rs = p.k_rs;
+    w.v_rs = p.v_rs;
+    w.o_rs = p.o_rs;
+    w.head_bytes = (uint32_t)(p.S - 1) * p.q_rs + W::ROW_BYTES;
+    w.kv_head_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * p.k_rs + W::ROW_BYTES : 0u;
+    w.v_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * p.v_rs + W::ROW_BYTES : 0u;
+    w.o_bytes = (uint32_t)(p.S - 1) * p.o_rs + W::ROW_BYTES;
+    w.kh = (const char*)p.k + (b * p.ksb + hh * p.ksh) * 2;
+    w.vh = (const char*)p.v + (b * p.vsb + hh * p.vsh) * 2;
+    w.oh = (const char*)p.o + (b * p.osb + hh * p.osh) * 2;
+    w.load_q((const char*)p.q + (b * p.qsb + hh * p.qsh) * 2);
+  } else {
+    const size_t kv_head_elems = (size_t)bh * p.Sk * D;
+    w.head_bytes = (uint32_t)p.S * W::ROW_BYTES;
+    w.kv_head_bytes = (uint32_t)p.Sk * W::ROW_BYTES;
+    w.kh = (const char*)p.k + kv_head_elems * 2;
+    w.vh = (const char*)p.v + kv_head_elems * 2;
+    w.load_q((const char*)p.q + head_elems * 2);
+  }
 
   // keys this work-group visits (causal: up to its last row's position)
   const int kv_end = CAUSAL ? min(p.Sk, q_lo + W::BM + p.shift) : p.Sk;
@@ -177,7 +195,7 @@ constexpr int kWaves = 8;
 template <int D>
 constexpr int key_tile() { return 64; }
 
-template <typename T, int D, bool CAUSAL, bool TAIL>
+template <typename T, int D, bool CAUSAL, bool TAIL, bool STRIDED>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   constexpr int BM = kWaves * 32;
   Params p;
@@ -192,17 +210,31 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   p.shift = a.causal ? a.Sk - a.S : 0;
   p.nqb = (a.S + BM - 1) / BM;
   p.c = a.scale * 1.4426950408889634f;
+  p.H = a.H;
+  if (STRIDED) {
+    const long long* st = a.strides;  // q, k, v, o: batch, head, row (elements)
+    p.qsb = st[0]; p.qsh = st[1]; p.q_rs = (uint32_t)(st[2] * 2);
+    p.ksb = st[3]; p.ksh = st[4]; p.k_rs = (uint32_t)(st[5] * 2);
+    p.vsb = st[6]; p.vsh = st[7]; p.v_rs = (uint32_t)(st[8] * 2);
+    p.osb = st[9]; p.osh = st[10]; p.o_rs = (uint32_t)(st[11] * 2);
+  }
   const long long grid = (long long)p.nqb * p.BH;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, key_tile<D>()>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, key_tile<D>(), STRIDED>), dim3((unsigned)grid),
+                     dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename T, int D, bool STRIDED>
+hipError_t launch_s(const FwdArgs& a, hipStream_t stream) {
+  const bool tail = a.Sk % key_tile<D>() != 0;
+  if (a.causal)
+    return tail ? launch_t<T, D, true, true, STRIDED>(a, stream) : launch_t<T, D, true, false, STRIDED>(a, stream);
+  return tail ? launch_t<T, D, false, true, STRIDED>(a, stream) : launch_t<T, D, false, false, STRIDED>(a, stream);
 }
 
 template <typename T, int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
-  const bool tail = a.Sk % key_tile<D>() != 0;
-  if (a.causal) return tail ? launch_t<T, D, true, true>(a, stream) : launch_t<T, D, true, false>(a, stream);
-  return tail ? launch_t<T, D, false, true>(a, stream) : launch_t<T, D, false, false>(a, stream);
+  return a.strides ? launch_s<T, D, true>(a, stream) : launch_s<T, D, false>(a, stream);
 }
 
 template <typename T>

@@ -16,7 +16,11 @@ namespace detail {
 // their Q fragments, running statistics and output accumulator, plus the
 // score tile / weights of the key tile in flight.  The work-group's NW
 // wavefronts share the K/V tiles (BN keys each) in LDS.
-template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
+//
+// Rows of a head are ROW_BYTES apart (dense [B][H][S][d] tensors), or, when
+// STRIDED, q_rs / k_rs / v_rs / o_rs bytes apart (e.g. a [B][S][H][d]
+// layout); the head bases and range sizes are set by the kernel either way.
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN, bool STRIDED = false>
 struct FwdWave {
   static constexpr int BM = NW * 32;
   static constexpr int ROW_BYTES = D * 2;
@@ -38,8 +42,17 @@ struct FwdWave {
   float c;   // scale * log2(e)
   const char* kh;
   const char* vh;
-  uint32_t head_bytes;     // one head of q / o
-  uint32_t kv_head_bytes;  // one head of k / v
+  uint32_t head_bytes;     // one head of q (and of o when dense)
+  uint32_t kv_head_bytes;  // one head of k (and of v when dense)
+  // STRIDED only: row strides in bytes, the v and o range sizes, o's head base
+  uint32_t q_rs, k_rs, v_rs, o_rs;
+  uint32_t v_bytes, o_bytes;
+  const char* oh;
+
+  __device__ __forceinline__ uint32_t q_row(int r) const { return (uint32_t)r * (STRIDED ? q_rs : ROW_BYTES); }
+  __device__ __forceinline__ uint32_t k_row(int r) const { return (uint32_t)r * (STRIDED ? k_rs : ROW_BYTES); }
+  __device__ __forceinline__ uint32_t v_row(int r) const { return (uint32_t)r * (STRIDED ? v_rs : ROW_BYTES); }
+  __device__ __forceinline__ uint32_t o_row(int r) const { return (uint32_t)r * (STRIDED ? o_rs : ROW_BYTES); }
 
   i16x8 qf[KSTEPS];
   f32x16 oacc[DB];
@@ -57,7 +70,7 @@ struct FwdWave {
     const __amdgpu_buffer_rsrc_t rq = rsrc(qh, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      const uint32_t off = (uint32_t)myq * ROW_BYTES + (kk * 16 + h * 8) * 2;
+      const uint32_t off = q_row(myq) + (kk * 16 + h * 8) * 2;
       qf[kk] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
 #pragma unroll
@@ -84,19 +97,19 @@ struct FwdWave {
   // Rows >= S read as 0 (buffer range check).
   __device__ __forceinline__ void issue_k(int tile, char* kd) const {
     const __amdgpu_buffer_rsrc_t rk = rsrc(kh, kv_head_bytes);
-    const uint32_t base = (uint32_t)tile * BN * ROW_BYTES;
+    const uint32_t base = k_row(tile * BN);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int f = i * NW + wave;  // block (sb, kk)
       const int ksb = f / KSTEPS, kk = f % KSTEPS;
-      const uint32_t off = base + (uint32_t)(ksb * 32 + (lane & 31)) * ROW_BYTES + (kk * 2 + (lane >> 5)) * 16;
+      const uint32_t off = base + k_row(ksb * 32 + (lane & 31)) + (kk * 2 + (lane >> 5)) * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + f * 1024), 16, off, 0, 0, 0);
     }
   }
 
   __device__ __forceinline__ void issue_v(int tile, char* vd) const {
-    const __amdgpu_buffer_rsrc_t rv = rsrc(vh, kv_head_bytes);
-    const uint32_t base = (uint32_t)tile * BN * ROW_BYTES;
+    const __amdgpu_buffer_rsrc_t rv = rsrc(vh, STRIDED ? v_bytes : kv_head_bytes);
+    const uint32_t base = v_row(tile * BN);
     const int x = lane >> 5;         // which half (d-block parity)
     const int lp = lane & 31;
     const int vg = lp >> 3;          // 16-lane group of the reading lanes 2lp, 2lp+1
@@ -106,7 +119,7 @@ struct FwdWave {
     for (int i = 0; i < LOADS; ++i) {
       const int f = i * NW + wave;  // block ((sb * 2 + cc) * 2 + tt) * (DB / 2) + dp
       const int dp = f % (DB / 2), rest = f / (DB / 2);
-      const uint32_t off = base + (uint32_t)(rest * 8 + vrow) * ROW_BYTES + (dp * 64 + vcol) * 2;
+      const uint32_t off = base + v_row(rest * 8 + vrow) + (dp * 64 + vcol) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + f * 1024), 16, off, 0, 0, 0);
     }
   }
@@ -253,7 +266,8 @@ struct FwdWave {
     const float ltot = sum_with_partner(lsum);
     const bool none = !(ltot > 0.f);
     const float inv = none ? 0.f : 1.0f / ltot;
-    const __amdgpu_buffer_rsrc_t ro = rsrc((const char*)o + head_elems * 2, head_bytes);
+    const __amdgpu_buffer_rsrc_t ro =
+        STRIDED ? rsrc(oh, o_bytes) : rsrc((const char*)o + head_elems * 2, head_bytes);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -262,7 +276,7 @@ struct FwdWave {
         w[0] = Elem<T>::pack(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv);
         w[1] = Elem<T>::pack(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv);
         const int dcol = db * 32 + 8 * rg + 4 * h;
-        __builtin_amdgcn_raw_buffer_store_b64(w, ro, (uint32_t)myq * ROW_BYTES + dcol * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(w, ro, o_row(myq) + dcol * 2, 0, 0);
       }
     if (h == 0) {
       const __amdgpu_buffer_rsrc_t rl = rsrc(lse + (size_t)bh * S, (uint32_t)S * 4);

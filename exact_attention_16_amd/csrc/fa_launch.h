@@ -18,6 +18,9 @@ struct FwdArgs {
   bool causal;
   float scale;
   int dtype;  // fa_dtype
+  // NULL: dense [B][H][S][d] tensors.  Else 12 element strides (host memory,
+  // read at launch): batch, head, row of q, k, v and o; d is contiguous.
+  const long long* strides;
 };
 
 // Number of work-groups the forward launch of `a` uses (for the host-side
@@ -66,6 +69,7 @@ struct DecodeArgs {
   bool causal;
   float scale;
   int dtype;  // fa_dtype
+  const long long* strides;  // as FwdArgs::strides (NULL: dense)
 };
 
 // Shape of the split-key pass for head dimension d: wavefronts per

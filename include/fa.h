@@ -42,11 +42,13 @@ enum {
   FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128                                   */
   FA_ERR_DTYPE = -4,     /* dtype is not an fa_dtype value                       */
   FA_ERR_SCALE = -5,     /* scale is NaN, infinite or negative                   */
-  FA_ERR_ALIGN = -6,     /* a tensor not 16-byte aligned, or lse/delta not 4-byte */
+  FA_ERR_ALIGN = -6,     /* a tensor (or a stride) not 16-byte aligned, or lse/delta not 4-byte */
   FA_ERR_ALIAS = -7,     /* an output overlaps an input or another output        */
   FA_ERR_TOO_LARGE = -8, /* S*d or Sk*d >= 2^30, or the grid exceeds 2^31-1      */
   FA_ERR_HIP = -9,       /* the HIP runtime rejected the launch (see below)      */
-  FA_ERR_WORKSPACE = -10 /* fa_fwd_decode: workspace missing, short or unaligned */
+  FA_ERR_WORKSPACE = -10, /* fa_fwd_decode: workspace missing, short or unaligned */
+  FA_ERR_STRIDE = -11    /* strided entry points: a stride negative, a row stride
+                            below d, or the output's strides not one-to-one   */
 };
 
 /*
@@ -110,6 +112,34 @@ int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse,
               int dtype, void* stream);
 
 /*
+ * fa_fwd_strided -- fa_fwd_kv on tensors with arbitrary batch, head and row
+ * strides (e.g. [B][S][H][d] "BSHD" tensors, or a slice of a larger key/value
+ * cache), so callers need not copy into the dense layout.
+ *
+ * strides: host array of 12 element strides, read during the call:
+ *     { q_batch, q_head, q_row,  k_batch, k_head, k_row,
+ *       v_batch, v_head, v_row,  o_batch, o_head, o_row }
+ * element (b, h, i, c) of q is at q + q_batch*b + q_head*h + q_row*i + c (in
+ * elements of `dtype`); d is always contiguous.  lse stays dense [B][H][Sq].
+ * Requirements (checked before any HIP call):
+ *   - strides >= 0 and multiples of 8 elements (16-byte rows), else
+ *     FA_ERR_STRIDE / FA_ERR_ALIGN;
+ *   - every row stride >= d, also for a single row (FA_ERR_STRIDE);
+ *   - o's strides map distinct positions to distinct elements
+ *     (FA_ERR_STRIDE);
+ *   - (rows + 512) * row_stride * 2 + 2d < 2^32 for every tensor
+ *     (32-bit offsets within a head, FA_ERR_TOO_LARGE);
+ *   - o and lse must not overlap the byte range any input spans
+ *     (FA_ERR_ALIAS; the inputs may overlap each other).
+ * Results are bitwise those of fa_fwd_kv on the same values in the dense
+ * layout.  Everything else as fa_fwd_kv.
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int H, int Sq, int Sk, int d,
+                   const long long* strides, int causal, float scale,
+                   int dtype, void* stream);
+
+/*
  * fa_fwd_decode -- fa_fwd_kv for a few queries over many keys (token-by-token
  * decoding), split over the keys.
  *
@@ -152,6 +182,19 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o,
  * size); then fa_fwd_decode needs no workspace or fails validation.
  */
 size_t fa_fwd_decode_workspace_size(int B, int H, int Sq, int Sk, int d);
+
+/*
+ * fa_fwd_decode_strided -- fa_fwd_decode on strided tensors (strides and
+ * their requirements as for fa_fwd_strided), e.g. the first Sk rows of a
+ * [B][S_max][H][d] key/value cache.  Results are bitwise those of
+ * fa_fwd_decode on the same values in the dense layout; the workspace size
+ * does not depend on the strides.
+ */
+int fa_fwd_decode_strided(const void* q, const void* k, const void* v, void* o,
+                          float* lse, int B, int H, int Sq, int Sk, int d,
+                          const long long* strides, int causal, float scale,
+                          int dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /*
  * fa_bwd -- enqueue the gradients of the exact-attention forward pass.

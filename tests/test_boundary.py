@@ -29,8 +29,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_workspace_size",
-                                   "fa_fwd_kv", "fa_last_hip_error", "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_strided",
+                                   "fa_fwd_decode_workspace_size", "fa_fwd_kv", "fa_fwd_strided",
+                                   "fa_last_hip_error", "fa_status_string", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in range(-10, 1):
+    for st in range(-11, 1):
         assert fa.fa_status_string(st)
     assert fa.fa_status_string(12345) == "unknown status"
     assert fa.fa_last_hip_error() == ""
@@ -189,3 +190,51 @@ def test_decode_validation_errors(lib, kw, status):
 def test_decode_empty_problem_is_a_no_op(lib):
     for dims in (dict(B=0), dict(H=0), dict(Sq=0)):
         assert call_dec(q=0, k=0, v=0, o=0, lse=0, ws=0, ws_bytes=0, **dims) == 0
+
+
+# fa_fwd_strided / fa_fwd_decode_strided: dense-equivalent strides by default
+D64 = [2 * 64 * 64, 64 * 64, 64]          # q, o: B=1, H=2, Sq=64, d=64
+K64 = [2 * 200 * 64, 200 * 64, 64]        # k, v: Sk=200
+
+
+def call_st(strides=None, **kw):
+    a = dict(GOOD_KV)
+    a.update(kw)
+    st = strides if strides is not None else D64 + K64 + K64 + D64
+    return fa.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Sq"], a["Sk"], a["d"],
+                             st, a["causal"], a["scale"], a["dtype"], None)
+
+
+def with_stride(i, value):
+    st = D64 + K64 + K64 + D64
+    st[i] = value
+    return st
+
+
+@pytest.mark.parametrize("strides,status", [
+    (with_stride(2, -64), -11), (with_stride(5, 32), -11), (with_stride(11, 0), -11),  # row stride < d
+    (with_stride(0, -1), -11),
+    (with_stride(1, 68), -6), (with_stride(8, 100), -6),                                 # not 16-byte rows
+    (with_stride(10, 64 * 32), -11),  # o's two heads overlap (head stride < 64 rows)
+    (with_stride(5, 1 << 22), -8),    # 32-bit row offsets exceeded
+])
+def test_strided_validation_errors(lib, strides, status):
+    assert call_st(strides) == status, fa.fa_status_string(status)
+
+
+def test_strided_null_and_alias(lib):
+    assert fa.fa_fwd_strided(Q, K, V, O, L, 1, 2, 64, 200, 64, None, 0, 0.125, fa.FA_DTYPE_BF16, None) == -1
+    # o placed inside k's strided extent (k spans 2*(200*64 + 199*64 + 64) bytes)
+    assert call_st(o=K + 4096) == -7
+    # a padded q row stride widens q's extent: an o right after the dense extent now overlaps
+    assert call_st(strides=[2 * 64 * 72, 64 * 72, 72] + K64 + K64 + D64, o=Q + 2 * 2 * 64 * 64) == -7
+
+
+def test_decode_strided_validation(lib):
+    st = D64 + K64 + K64 + D64
+    bad = list(st)
+    bad[5] = 8
+    args = (Q, K, V, O, L, 1, 2, 64, 200, 64)
+    assert fa.fa_fwd_decode_strided(*args, bad, 0, 0.125, fa.FA_DTYPE_BF16, WS, 1 << 20, None) == -11
+    assert fa.fa_fwd_decode_strided(*args, st, 0, 0.125, fa.FA_DTYPE_BF16, 0, 0, None) == -10
+    assert fa.fa_fwd_decode_strided(*args, None, 0, 0.125, fa.FA_DTYPE_BF16, WS, 1 << 20, None) == -1

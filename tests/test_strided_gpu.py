@@ -1,0 +1,132 @@
+"""GPU parity of the strided entry points (fa_fwd_strided, fa_fwd_decode_strided)
+through the C ABI.
+
+The strided kernels do the dense kernels' arithmetic in the same order, only
+addressing rows through the caller's strides, so on the same values they must
+give BITWISE the dense results; small cases are also compared with the fp64
+oracle.  Layouts: [B, S, H, d] ("BSHD") storage viewed as [B, H, S, d], the
+first Sk rows of a larger key/value cache, padded rows, mixed layouts, and an
+output written into a view of a larger buffer whose other elements must stay
+untouched.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_16_amd as fa
+import oracle
+from exact_attention_16_amd.inputs import default_scale, make_inputs_kv
+from tests.gpu_helpers import TOL_LSE, TOL_O, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def bshd(x):
+    """The same values stored [B, S, H, d], returned as a [B, H, S, d] view."""
+    return x.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+def padded(x, pad=8):
+    """The same values with every row padded by `pad` elements."""
+    B, H, S, d = x.shape
+    buf = torch.full((B, H, S, d + pad), float("nan"), dtype=x.dtype, device=x.device)
+    buf[..., :d] = x
+    return buf[..., :d]
+
+
+def cache_slice(x, extra=37):
+    """The same values as the first S rows of a [B, S + extra, H, d] cache."""
+    B, H, S, d = x.shape
+    cache = torch.randn(B, S + extra, H, d, device=x.device).to(x.dtype)
+    cache[:, :S] = x.transpose(1, 2)
+    return cache[:, :S].transpose(1, 2)
+
+
+LAYOUTS = {"bshd": bshd, "padded": padded, "cache": cache_slice}
+
+
+def check_oracle(o, lse, q, k, v, causal, scale, label):
+    o_ref, l_ref = oracle.attention_kv(to64(q.cpu()), to64(k.cpu()), to64(v.cpu()), causal, scale, workers=8)
+    o = o.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    live = np.isfinite(l_ref)
+    eo = float(np.max(np.abs(o - o_ref)))
+    el = float(np.max(np.abs(lse[live] - l_ref[live]))) if live.any() else 0.0
+    print(f"{label}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+@pytest.mark.parametrize("Sq,Sk", [(300, 300), (100, 333), (333, 100), (1, 257)])
+def test_forward_strided_equals_dense(Sq, Sk, layout, d, causal):
+    q, k, v = (x.cuda() for x in make_inputs_kv(2, 3, Sq, Sk, d, "bf16", seed=90_000 + Sq + 7 * Sk + d))
+    scale = default_scale(d)
+    label = f"strided fwd {layout} Sq={Sq} Sk={Sk} d={d} causal={causal}"
+    say(label)
+    o_dense, l_dense = fa.forward(q, k, v, causal=causal, scale=scale)
+    f = LAYOUTS[layout]
+    qs, ks, vs = f(q), f(k), f(v)
+    assert not (qs.is_contiguous() and ks.is_contiguous())
+    o, lse = fa.forward(qs, ks, vs, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    if layout == "bshd" and Sq > 1:
+        assert o.stride() == qs.stride()  # a default out takes q's (dense) layout
+    assert torch.equal(o, o_dense) and torch.equal(lse, l_dense), label
+    check_oracle(o, lse, q, k, v, causal, scale, label)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Sq,Sk", [(1, 4097), (3, 1000), (40, 2500)])
+def test_decode_strided_equals_dense(Sq, Sk, d, causal):
+    """Decoding over the first Sk rows of a [B, S_max, H, d] cache, with q and
+    o in [B, S, H, d] storage."""
+    q, k, v = (x.cuda() for x in make_inputs_kv(2, 4, Sq, Sk, d, "bf16", seed=91_000 + Sq + Sk + d))
+    scale = default_scale(d)
+    label = f"strided decode Sq={Sq} Sk={Sk} d={d} causal={causal}"
+    say(label)
+    o_dense, l_dense = fa.decode(q, k, v, causal=causal, scale=scale)
+    o, lse = fa.decode(bshd(q), cache_slice(k), cache_slice(v), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_dense) and torch.equal(lse, l_dense), label
+    check_oracle(o, lse, q, k, v, causal, scale, label)
+
+
+def test_output_view_leaves_the_rest_untouched():
+    """o written through a [B, S, H, d] view of a buffer with an extra head and
+    padded rows: only the viewed elements change."""
+    q, k, v = (x.cuda() for x in make_inputs_kv(2, 3, 200, 200, 64, "fp16", seed=92_000))
+    say("strided output view")
+    buf = torch.full((2, 200, 4, 72), 1234.0, dtype=torch.float16, device="cuda")
+    out = buf[:, :, 1:, :64].transpose(1, 2)  # [2, 3, 200, 64] view
+    o, lse = fa.forward(q, k, v, causal=True, out=out)
+    o_dense, l_dense = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_dense) and torch.equal(lse, l_dense)
+    mask = torch.ones_like(buf, dtype=torch.bool)
+    mask[:, :, 1:, :64] = False
+    assert (buf[mask] == 1234.0).all().item()
+
+
+def test_large_bshd_bitwise():
+    """The long causal workload's shape in BSHD storage: bitwise the dense result."""
+    q, k, v = (x.cuda() for x in make_inputs_kv(2, 16, 8192, 8192, 128, "bf16", seed=93_000))
+    say("strided large bshd")
+    o_dense, l_dense = fa.forward(q, k, v, causal=True)
+    o, lse = fa.forward(bshd(q), bshd(k), bshd(v), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_dense) and torch.equal(lse, l_dense)
+
+
+def test_strided_binding_errors():
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):  # head dimension not contiguous
+        fa.forward(q.transpose(2, 3).contiguous().transpose(2, 3), q, q)
+    buf = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    overlapped = buf.as_strided((1, 2, 8, 64), (1024, 0, 64, 1))  # both heads on one slab
+    with pytest.raises(fa.FaError) as e:
+        fa.forward(q, q, q, out=overlapped)
+    assert e.value.status == fa.FA_ERR_STRIDE
