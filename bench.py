@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-per-config] [--no-sweep]
-                    [--no-backward] [--no-decode] [--copy-calibration]
+                    [--no-backward] [--no-decode] [--no-wide] [--decode NAMES]
+                    [--copy-calibration]
 
 One step is one exact-attention forward pass (every step of the method, one
 kernel launch) over one batch of the workload's synthetic inputs, already
@@ -11,7 +12,8 @@ resident in device memory.  The default workload is the short-sequence batch
 also timed and reported under "per_config", the pages' benchmark grid
 (S 512..16k x d 64/128 x causal, 16k tokens, bf16) under "sweep", and the
 gradients (fa_bwd) of the five workloads under "backward", and the split-key
-decoding pass (fa_fwd_decode) over three 1 GiB K/V caches under "decode".
+decoding pass (fa_fwd_decode) over three 1 GiB K/V caches under "decode", and
+wide heads (d = 192, 256) under "wide".
 Rank 0 prints ONE JSON line.
 
 The timed region is bracketed by torch.cuda.synchronize(); the launches go on
@@ -236,6 +238,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the S x d x causal grid")
     ap.add_argument("--no-backward", action="store_true", help="skip the gradient timings")
     ap.add_argument("--no-decode", action="store_true", help="skip the split-key decoding timings")
+    ap.add_argument("--no-wide", action="store_true", help="skip the wide-head (d = 192, 256) timings")
     ap.add_argument("--decode", default="", help="comma-separated decoding workloads (default: all)")
     ap.add_argument("--cpu-heads", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -250,7 +253,7 @@ def main():
     import torch
 
     import exact_attention_16_amd as fa
-    from exact_attention_16_amd.inputs import DECODE, SWEEP, WORKLOADS, WORKLOADS_BY_NAME
+    from exact_attention_16_amd.inputs import DECODE, SWEEP, WIDE, WORKLOADS, WORKLOADS_BY_NAME
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -315,6 +318,8 @@ def main():
     # The pages' kernel-benchmark grid (S 512..16k x d 64/128 x causal, 16k
     # tokens per batch), bf16.
     sweep = [] if args.no_sweep else time_list(SWEEP)
+    # Wide heads (d = 192, 256: four-wavefront work-groups), beyond the grid.
+    wide = [] if args.no_wide else time_list(WIDE)
     # Token-by-token decoding (fa_fwd_decode: split pass + merge per step),
     # bound by HBM: reported against the 8 TB/s peak.
     decode = []
@@ -360,6 +365,7 @@ def main():
         "sweep": sweep,
         "backward": backward,
         "decode": decode,
+        "wide": wide,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
         "wall_s_timed_region": r["wall_s"],

@@ -25,7 +25,8 @@ ARCH = "gfx950"
 # canonicalisation that otherwise doubles the row-max instructions (NaN
 # inputs give unspecified results).  The host front end keeps IEEE semantics
 # for its argument checks (isfinite on the scale).
-SOURCES = [("fa_api.cpp", []), ("fa_fwd.hip", ["-fno-honor-nans"]), ("fa_bwd.hip", ["-fno-honor-nans"]), ("fa_decode.hip", ["-fno-honor-nans"])]
+SOURCES = [("fa_api.cpp", []), ("fa_fwd.hip", ["-fno-honor-nans"]), ("fa_bwd.hip", ["-fno-honor-nans"]), ("fa_decode.hip", ["-fno-honor-nans"]),
+           ("fa_fwd_wide.hip", ["-fno-honor-nans"])]
 COMMON = ["-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function"]

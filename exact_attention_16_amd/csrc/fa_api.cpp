@@ -14,6 +14,9 @@ namespace {
 
 thread_local char g_last_hip_error[256] = "";
 
+// Head dimensions of the forward and decoding kernels (the backward: 64, 128).
+bool forward_head_dim(int d) { return d == 64 || d == 128 || d == 192 || d == 256; }
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
@@ -74,7 +77,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
              int S, int Sk, int d, int causal, float scale, int dtype, const long long* strides = nullptr,
              bool strided = false, Extents* ext = nullptr) {
   if (B < 0 || H < 0 || S < 0 || Sk < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!forward_head_dim(d)) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   if ((long long)B * H * S == 0) return FA_OK;  // empty problem: nothing to touch
@@ -219,7 +222,7 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
 }
 
 size_t fa_fwd_decode_workspace_size(int B, int H, int Sq, int Sk, int d) {
-  if (B <= 0 || H <= 0 || Sq <= 0 || Sk < 0 || (d != 64 && d != 128)) return 0;
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk < 0 || !forward_head_dim(d)) return 0;
   fa::DecodeArgs a{};
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
   return fa::decode_plan(a).workspace_bytes;
@@ -258,7 +261,7 @@ const char* fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a pointer argument is NULL";
     case FA_ERR_SHAPE: return "B, H, S or Sk is negative, or causal is not 0 or 1";
-    case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_HEAD_DIM: return "head dimension d must be 64, 128, 192 or 256 (fa_bwd: 64 or 128)";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
     case FA_ERR_ALIGN:

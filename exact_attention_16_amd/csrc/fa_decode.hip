@@ -352,6 +352,16 @@ hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& plan, hipStrea
   return a.strides ? launch_decode_s<T, D, true>(a, plan, stream) : launch_decode_s<T, D, false>(a, plan, stream);
 }
 
+template <typename T>
+hipError_t launch_decode_dt(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
+  switch (a.d) {
+    case 64: return launch_decode_d<T, 64>(a, plan, stream);
+    case 128: return launch_decode_d<T, 128>(a, plan, stream);
+    case 192: return launch_decode_d<T, 192>(a, plan, stream);
+    default: return launch_decode_d<T, 256>(a, plan, stream);
+  }
+}
+
 }  // namespace detail
 
 using namespace detail;
@@ -380,8 +390,8 @@ DecodePlan decode_plan(const DecodeArgs& a) {
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
   if (a.dtype == 1)
-    return a.d == 64 ? launch_decode_d<__bf16, 64>(a, plan, stream) : launch_decode_d<__bf16, 128>(a, plan, stream);
-  return a.d == 64 ? launch_decode_d<_Float16, 64>(a, plan, stream) : launch_decode_d<_Float16, 128>(a, plan, stream);
+    return launch_decode_dt<__bf16>(a, plan, stream);
+  return launch_decode_dt<_Float16>(a, plan, stream);
 }
 
 }  // namespace fa

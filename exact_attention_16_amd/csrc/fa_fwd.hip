@@ -96,68 +96,15 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
   w.col = w.lane & 31;
   const int group = w.wave >> 2;
 
-  // Work-group -> (query block, head).  The dispatcher deals work-group ids
-  // to the chip's XCDs round-robin (id % kXcds), each XCD with its own L2.
-  // When B*H is a multiple of kXcds, the ids an XCD receives are remapped so
-  // that all of one head's query blocks run on one XCD.  Non-causal: an XCD
-  // runs a head's query blocks back to back; they stream the same K/V tiles
-  // at about the same time, so each tile comes from HBM once per head.
-  // Causal: query block qb visits qb + 1 row blocks' worth of key tiles, so
-  // an XCD's queue is ordered longest first across its heads (all heads'
-  // last query blocks, then the next-to-last, ...) and the short blocks fill
-  // the tail (greedy longest-processing-time scheduling).
   int bh, qb;
-  if (p.BH % kXcds == 0) {
-    const int local = blockIdx.x / kXcds;  // position in this XCD's queue
-    if (CAUSAL) {
-      const int heads_per_xcd = p.BH / kXcds;
-      qb = local / heads_per_xcd;
-      bh = (local % heads_per_xcd) * kXcds + blockIdx.x % kXcds;
-    } else {
-      qb = local % p.nqb;
-      bh = (local / p.nqb) * kXcds + blockIdx.x % kXcds;
-    }
-  } else {
-    qb = blockIdx.x % p.nqb;
-    bh = blockIdx.x / p.nqb;
-  }
-  if (CAUSAL) qb = p.nqb - 1 - qb;
+  map_query_block<CAUSAL>(blockIdx.x, p.BH, p.nqb, bh, qb);
   const int q_lo = qb * W::BM;
   // Row blocks alternate between the groups (group 0: blocks 0, 2, 4, 6;
   // group 1: 1, 3, 5, 7), so near the causal diagonal both groups still have
   // about the same number of key tiles and neither idles beside the other.
   w.qw = q_lo + 32 * (2 * (w.wave & 3) + group);
   w.myq = w.qw + w.col;
-  w.S = p.S;
-  w.Sk = p.Sk;
-  w.shift = p.shift;
-  w.c = p.c;
-
-  const size_t head_elems = (size_t)bh * p.S * D;
-  if constexpr (STRIDED) {
-    // head bases from the batch and head strides; each range ends with the
-    // head's last row, so rows past S (or Sk) read as 0 / are dropped
-    const int b = bh / p.H, hh = bh - b * p.H;
-    w.q_rs = p.q_rs;
-    w.k_rs = p.k_rs;
-    w.v_rs = p.v_rs;
-    w.o_rs = p.o_rs;
-    w.head_bytes = (uint32_t)(p.S - 1) * p.q_rs + W::ROW_BYTES;
-    w.kv_head_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * p.k_rs + W::ROW_BYTES : 0u;
-    w.v_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * p.v_rs + W::ROW_BYTES : 0u;
-    w.o_bytes = (uint32_t)(p.S - 1) * p.o_rs + W::ROW_BYTES;
-    w.kh = (const char*)p.k + (b * p.ksb + hh * p.ksh) * 2;
-    w.vh = (const char*)p.v + (b * p.vsb + hh * p.vsh) * 2;
-    w.oh = (const char*)p.o + (b * p.osb + hh * p.osh) * 2;
-    w.load_q((const char*)p.q + (b * p.qsb + hh * p.qsh) * 2);
-  } else {
-    const size_t kv_head_elems = (size_t)bh * p.Sk * D;
-    w.head_bytes = (uint32_t)p.S * W::ROW_BYTES;
-    w.kv_head_bytes = (uint32_t)p.Sk * W::ROW_BYTES;
-    w.kh = (const char*)p.k + kv_head_elems * 2;
-    w.vh = (const char*)p.v + kv_head_elems * 2;
-    w.load_q((const char*)p.q + head_elems * 2);
-  }
+  const size_t head_elems = w.setup(p, bh);
 
   // keys this work-group visits (causal: up to its last row's position)
   const int kv_end = CAUSAL ? min(p.Sk, q_lo + W::BM + p.shift) : p.Sk;
@@ -247,11 +194,13 @@ hipError_t launch_dtype(const FwdArgs& a, hipStream_t stream) {
 using namespace detail;
 
 long long fwd_grid_size(const FwdArgs& a) {
+  if (a.d > 128) return fwd_wide_grid_size(a);
   const int BM = kWaves * 32;
   return (long long)((a.S + BM - 1) / BM) * a.B * a.H;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  if (a.d > 128) return launch_fwd_wide(a, stream);  // fa_fwd_wide.hip
   // dtype 0 = fp16, 1 = bf16 (fa_dtype)
   return a.dtype == 1 ? launch_dtype<__bf16>(a, stream) : launch_dtype<_Float16>(a, stream);
 }

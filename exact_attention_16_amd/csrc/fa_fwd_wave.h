@@ -12,6 +12,35 @@
 namespace fa {
 namespace detail {
 
+// Work-group -> (query block, head).  The dispatcher deals work-group ids to
+// the chip's XCDs round-robin (id % kXcds), each XCD with its own L2.  When
+// B*H is a multiple of kXcds, the ids an XCD receives are remapped so that
+// all of one head's query blocks run on one XCD.  Non-causal: an XCD runs a
+// head's query blocks back to back; they stream the same K/V tiles at about
+// the same time, so each tile comes from HBM once per head.  Causal: query
+// block qb visits qb + 1 row blocks' worth of key tiles, so an XCD's queue
+// is ordered longest first across its heads (all heads' last query blocks,
+// then the next-to-last, ...) and the short blocks fill the tail (greedy
+// longest-processing-time scheduling).
+template <bool CAUSAL>
+__device__ __forceinline__ void map_query_block(unsigned id, int BH, int nqb, int& bh, int& qb) {
+  if (BH % kXcds == 0) {
+    const int local = id / kXcds;  // position in this XCD's queue
+    if (CAUSAL) {
+      const int heads_per_xcd = BH / kXcds;
+      qb = local / heads_per_xcd;
+      bh = (local % heads_per_xcd) * kXcds + id % kXcds;
+    } else {
+      qb = local % nqb;
+      bh = (local / nqb) * kXcds + id % kXcds;
+    }
+  } else {
+    qb = id % nqb;
+    bh = id / nqb;
+  }
+  if (CAUSAL) qb = nqb - 1 - qb;
+}
+
 // One wavefront's share of a work-group: 32 query rows of one (batch, head),
 // their Q fragments, running statistics and output accumulator, plus the
 // score tile / weights of the key tile in flight.  The work-group's NW
@@ -61,6 +90,42 @@ struct FwdWave {
   float m_used;      // reference max (raw score units) the weights are taken against
   float mc;          // c * m_used
   float lsum;        // this lane's share of the row sum
+
+  // Lengths, scale, the head's Q/K/V/O bases and ranges from the launch
+  // parameters, then this lane's Q row (qw, myq and the lane fields must be
+  // set).  Returns the dense head offset in elements (bh * S * D).
+  __device__ __forceinline__ size_t setup(const Params& p, int bh) {
+    S = p.S;
+    Sk = p.Sk;
+    shift = p.shift;
+    c = p.c;
+    const size_t head_elems = (size_t)bh * p.S * D;
+    if constexpr (STRIDED) {
+      // head bases from the batch and head strides; each range ends with the
+      // head's last row, so rows past S (or Sk) read as 0 / are dropped
+      const int b = bh / p.H, hh = bh - b * p.H;
+      q_rs = p.q_rs;
+      k_rs = p.k_rs;
+      v_rs = p.v_rs;
+      o_rs = p.o_rs;
+      head_bytes = (uint32_t)(p.S - 1) * p.q_rs + ROW_BYTES;
+      kv_head_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * p.k_rs + ROW_BYTES : 0u;
+      v_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * p.v_rs + ROW_BYTES : 0u;
+      o_bytes = (uint32_t)(p.S - 1) * p.o_rs + ROW_BYTES;
+      kh = (const char*)p.k + (b * p.ksb + hh * p.ksh) * 2;
+      vh = (const char*)p.v + (b * p.vsb + hh * p.vsh) * 2;
+      oh = (const char*)p.o + (b * p.osb + hh * p.osh) * 2;
+      load_q((const char*)p.q + (b * p.qsb + hh * p.qsh) * 2);
+    } else {
+      const size_t kv_head_elems = (size_t)bh * p.Sk * D;
+      head_bytes = (uint32_t)p.S * ROW_BYTES;
+      kv_head_bytes = (uint32_t)p.Sk * ROW_BYTES;
+      kh = (const char*)p.k + kv_head_elems * 2;
+      vh = (const char*)p.v + kv_head_elems * 2;
+      load_q((const char*)p.q + head_elems * 2);
+    }
+    return head_elems;
+  }
 
   // Does this wavefront have any unmasked key in the tile starting at k0?
   __device__ __forceinline__ bool active(int k0) const { return !(CAUSAL && k0 > qw + 31 + shift); }
@@ -138,6 +203,11 @@ struct FwdWave {
       for (int sb = 0; sb < SB; ++sb) kf[sb] = *(const i16x8*)(ks + (sb * KSTEPS + kk) * 1024 + lane * 16);
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) sacc[sb] = Elem<T>::mma(kf[sb], qf[kk], sacc[sb]);
+      // wide heads: keep the scheduler from hoisting every k-step's LDS reads
+      // to the top (they would not fit the register file); four k-steps of
+      // reads may run ahead of the MFMAs
+      if constexpr (D > 128)
+        if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -167,6 +237,8 @@ struct FwdWave {
           oacc[db] = Elem<T>::mma(vf, pf[sb][cc], oacc[db]);
         }
       }
+      if constexpr (D > 128)  // as in scores(): bound the reads in flight
+        if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
   }
 

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI front end (fa_api.cpp) and the gfx950
-// kernels (fa_fwd.hip, fa_bwd.hip, fa_decode.hip).  Not installed; callers use
+// kernels (fa_fwd.hip, fa_fwd_wide.hip, fa_bwd.hip, fa_decode.hip).  Not
+// installed; callers use
 // include/fa.h.
 #pragma once
 
@@ -29,6 +30,11 @@ long long fwd_grid_size(const FwdArgs& a);
 
 // Enqueue the forward kernels on `stream`; returns the launch status.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// The same for head dimensions 192 and 256 (fa_fwd_wide.hip), used by the two
+// functions above.
+long long fwd_wide_grid_size(const FwdArgs& a);
+hipError_t launch_fwd_wide(const FwdArgs& a, hipStream_t stream);
 
 struct BwdArgs {
   const void* q;

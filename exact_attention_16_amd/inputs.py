@@ -151,3 +151,11 @@ DECODE = (
     DecodeWorkload("decode_B1_S131072_d128", 1, 16, 1, 131072, 128, "bf16", True, 3003),
 )
 DECODE_BY_NAME = {w.name: w for w in DECODE}
+
+# Wide heads (d = 192, 256; beyond the pages' grid): the grid's 16k tokens at
+# S = 4096 with 8 heads, bf16.
+WIDE = (
+    Workload("wide_S4096_d256_full", 4, 8, 4096, 256, "bf16", False, 3101),
+    Workload("wide_S4096_d256_causal", 4, 8, 4096, 256, "bf16", True, 3102),
+    Workload("wide_S4096_d192_full", 4, 8, 4096, 192, "bf16", False, 3103),
+)

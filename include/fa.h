@@ -39,7 +39,7 @@ enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a pointer argument is NULL (non-empty problem)       */
   FA_ERR_SHAPE = -2,     /* B, H, S or Sk negative, or causal not 0/1            */
-  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128                                   */
+  FA_ERR_HEAD_DIM = -3,  /* d not 64/128/192/256 (fa_bwd: not 64/128)          */
   FA_ERR_DTYPE = -4,     /* dtype is not an fa_dtype value                       */
   FA_ERR_SCALE = -5,     /* scale is NaN, infinite or negative                   */
   FA_ERR_ALIGN = -6,     /* a tensor (or a stride) not 16-byte aligned, or lse/delta not 4-byte */
@@ -62,7 +62,9 @@ enum {
  *   B, H, S  batch, heads, sequence length (query length = key length).
  *            B*H*S == 0 is an empty problem: nothing is read or written and
  *            FA_OK is returned (pointers may then be NULL).
- *   d        head dimension: 64 or 128 (the pages' benchmark head sizes).
+ *   d        head dimension: 64 or 128 (the pages' benchmark head sizes), or
+ *            192 or 256 (wide heads: four wavefronts of 32 query rows per
+ *            work-group, one per SIMD, instead of eight).
  *   causal   0 = no mask; 1 = keep key j for query i iff j <= i.
  *   scale    multiplies every score before the softmax; must be finite and
  *            >= 0 (0 gives uniform weights).  Callers normally pass

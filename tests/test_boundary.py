@@ -66,7 +66,7 @@ def call(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1), (dict(lse=0), -1),
     (dict(B=-1), -2), (dict(H=-3), -2), (dict(S=-1), -2), (dict(causal=2), -2),
-    (dict(d=32), -3), (dict(d=96), -3), (dict(d=256), -3), (dict(d=0), -3),
+    (dict(d=32), -3), (dict(d=96), -3), (dict(d=320), -3), (dict(d=0), -3),
     (dict(dtype=2), -4), (dict(dtype=-1), -4),
     (dict(scale=float("nan")), -5), (dict(scale=float("inf")), -5), (dict(scale=-0.5), -5),
     (dict(q=Q + 8), -6), (dict(v=V + 2), -6), (dict(o=O + 4), -6), (dict(lse=L + 2), -6),
@@ -103,7 +103,7 @@ def call_bwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), -1), (dict(o=0), -1), (dict(lse=0), -1), (dict(dout=0), -1), (dict(dq=0), -1),
     (dict(dk=0), -1), (dict(dv=0), -1), (dict(delta=0), -1),
-    (dict(B=-1), -2), (dict(causal=3), -2), (dict(d=80), -3), (dict(dtype=7), -4),
+    (dict(B=-1), -2), (dict(causal=3), -2), (dict(d=80), -3), (dict(d=256), -3), (dict(dtype=7), -4),
     (dict(scale=float("nan")), -5), (dict(scale=-1.0), -5),
     (dict(dout=BDO + 8), -6), (dict(dq=BDQ + 2), -6), (dict(delta=BDL + 2), -6), (dict(lse=BL_ + 1), -6),
     (dict(dq=BQ_), -7), (dict(dk=BO_ + 64), -7), (dict(dv=BDO + 4096), -7), (dict(delta=BL_), -7),
@@ -170,6 +170,7 @@ def test_decode_workspace_size_is_a_pure_function(lib):
     # grows with the query rows and the heads; 0 for empty or invalid shapes
     assert fa.fa_fwd_decode_workspace_size(1, 2, 128, 200, 64) > n
     assert fa.fa_fwd_decode_workspace_size(2, 2, 64, 200, 64) > n
+    assert fa.fa_fwd_decode_workspace_size(1, 2, 64, 200, 256) > n  # fp32 partials grow with d
     for bad in ((0, 2, 64, 200, 64), (1, 2, 0, 200, 64), (1, 2, 64, -1, 64), (1, 2, 64, 200, 80),
                 (-1, 2, 64, 200, 64)):
         assert fa.fa_fwd_decode_workspace_size(*bad) == 0
