@@ -193,6 +193,11 @@ struct FwdWave {
   // per 32-key block (keys 8*(r/4) + 4*h + r%4 of the block, r = 0..15).
   // The k-steps run in the outer loop so the SB accumulation chains
   // interleave instead of waiting on one another.
+  // K fragment (A operand of S^T) of 32-key block sb, k-step kk.
+  __device__ __forceinline__ i16x8 k_frag(const char* ks, int sb, int kk) const {
+    return *(const i16x8*)(ks + (sb * KSTEPS + kk) * 1024 + lane * 16);
+  }
+
   __device__ __forceinline__ void scores(const char* ks) {
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) sacc[sb] = f32x16{};
@@ -200,7 +205,7 @@ struct FwdWave {
     for (int kk = 0; kk < KSTEPS; ++kk) {
       i16x8 kf[SB];
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb) kf[sb] = *(const i16x8*)(ks + (sb * KSTEPS + kk) * 1024 + lane * 16);
+      for (int sb = 0; sb < SB; ++sb) kf[sb] = k_frag(ks, sb, kk);
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) sacc[sb] = Elem<T>::mma(kf[sb], qf[kk], sacc[sb]);
       // wide heads: keep the scheduler from hoisting every k-step's LDS reads
@@ -219,6 +224,19 @@ struct FwdWave {
   // (e = 0..3); the V block layout puts there
   // V[32*sb + 16*cc + 8*tt + 4*(g/2) + e][32*db + 16*(g%2) + j] for group g,
   // i.e. lane l receives V^T[d = 32*db + l%32][its 4 keys].
+  // V^T fragment (A operand of O^T += V^T P^T) of d-block db, key chunk
+  // (sb, cc).
+  __device__ __forceinline__ i16x8 v_frag(const char* vs, int db, int sb, int cc) const {
+    i16x4 half[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int blk = ((sb * 2 + cc) * 2 + tt) * (DB / 2) + (db >> 1);
+      const char* a = vs + blk * 1024 + (db & 1) * 512 + lane * 8;
+      half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
+    }
+    return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+
   __device__ __forceinline__ void pv(const char* vs) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -226,14 +244,7 @@ struct FwdWave {
       for (int sb = 0; sb < SB; ++sb) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          i16x4 half[2];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int blk = ((sb * 2 + cc) * 2 + tt) * (DB / 2) + (db >> 1);
-            const char* a = vs + blk * 1024 + (db & 1) * 512 + lane * 8;
-            half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
-          }
-          const i16x8 vf = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const i16x8 vf = v_frag(vs, db, sb, cc);
           oacc[db] = Elem<T>::mma(vf, pf[sb][cc], oacc[db]);
         }
       }
@@ -254,7 +265,12 @@ struct FwdWave {
   }
 
   template <bool MASKED>
-  __device__ __forceinline__ void softmax_impl(int k0) {
+  __device__ __forceinline__ void softmax_impl(int k0) { softmax_on<MASKED>(k0, sacc); }
+
+  // The update on scores held in `sacc` (this wavefront's own, or a second
+  // score buffer of a pipelined schedule).
+  template <bool MASKED>
+  __device__ __forceinline__ void softmax_on(int k0, f32x16 (&sacc)[SB]) {
     if (MASKED) {
       // key k0 + t + 4h (t below) is kept iff t < Sk - k0 - 4h and, when
       // causal, t <= myq + shift - k0 - 4h
