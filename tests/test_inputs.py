@@ -84,3 +84,29 @@ def test_fp16_cast_is_round_to_nearest_even():
     x = torch.randn(1_000_000, generator=torch.Generator().manual_seed(4)) * 4
     got = x.to(torch.float16).numpy()
     np.testing.assert_array_equal(got, x.numpy().astype(np.float16))
+
+
+def test_separate_length_inputs():
+    from exact_attention_16_amd.inputs import make_inputs_kv
+
+    q, k, v = make_inputs_kv(2, 3, 5, 17, 64, "bf16", seed=7)
+    assert q.shape == (2, 3, 5, 64) and k.shape == v.shape == (2, 3, 17, 64)
+    assert q.dtype == k.dtype == v.dtype == torch.bfloat16
+    # the same recipe as make_inputs: draws in the order Q, K, V
+    g = torch.Generator().manual_seed(7)
+    rq = torch.randn((2, 3, 5, 64), generator=g).to(torch.bfloat16)
+    rk = torch.randn((2, 3, 17, 64), generator=g).to(torch.bfloat16)
+    assert torch.equal(q, rq) and torch.equal(k, rk)
+    q2, _, _ = make_inputs_kv(2, 3, 5, 17, 64, "bf16", seed=7)
+    assert torch.equal(q, q2)
+
+
+def test_decoding_and_wide_workloads():
+    from exact_attention_16_amd.inputs import DECODE, WIDE
+
+    for w in DECODE:
+        assert w.Sq == 1 and w.causal and w.dtype == "bf16"
+        assert w.H * w.d == 2048                              # the grid's model width
+        assert w.B * w.H * w.Sk * w.d * 2 * 2 == 1 << 30      # 1 GiB of K and V
+    for w in WIDE:
+        assert w.d in (192, 256) and w.B * w.S == 16384
