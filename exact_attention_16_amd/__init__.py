@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     backward,
     decode,
     fa_bwd,
+    fa_bwd_strided,
     fa_fwd,
     fa_fwd_decode,
     fa_fwd_decode_strided,

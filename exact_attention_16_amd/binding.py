@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
             lib.fa_fwd_decode_workspace_size.restype = ctypes.c_size_t
             lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
             lib.fa_bwd.restype = i
+            lib.fa_bwd_strided.argtypes = [vp] * 10 + [i, i, i, i, vp, i, f, i, vp]
+            lib.fa_bwd_strided.restype = i
             lib.fa_status_string.argtypes = [i]
             lib.fa_status_string.restype = ctypes.c_char_p
             lib.fa_last_hip_error.argtypes = []
@@ -101,10 +103,10 @@ def fa_fwd_decode(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, worksp
 
 
 def _strides_arg(strides):
-    """12 element strides as a host int64 array (None stays NULL)."""
+    """Element strides as a host int64 array (None stays NULL)."""
     if strides is None:
         return None
-    arr = (ctypes.c_longlong * 12)(*[int(x) for x in strides])
+    arr = (ctypes.c_longlong * len(strides))(*[int(x) for x in strides])
     return ctypes.cast(arr, ctypes.c_void_p), arr  # keep arr alive with the pointer
 
 
@@ -135,6 +137,16 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, 
                                       int(causal), float(scale), int(dtype), stream))
 
 
+def fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, strides, causal, scale, dtype,
+                   stream) -> int:
+    """The C entry point; ``strides`` is a sequence of 24 element strides (q, k,
+    v, o, dout, dq, dk, dv: batch, head, row) or None; returns the status."""
+    arg = _strides_arg(strides)
+    return int(load_library().fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, delta, int(B), int(H), int(S),
+                                              int(d), arg[0] if arg else None, int(causal), float(scale),
+                                              int(dtype), stream))
+
+
 class FaError(RuntimeError):
     def __init__(self, status: int, entry: str = "fa_fwd"):
         msg = fa_status_string(status)
@@ -144,15 +156,14 @@ class FaError(RuntimeError):
         self.status = status
 
 
-def _layout(q, k, v, o):
-    """None when q, k, v and o are all contiguous; else their 12 element
-    strides (batch, head, row each) for the strided entry points, which need
-    the head dimension contiguous."""
-    ts = (q, k, v, o)
+def _layout(*ts):
+    """None when all tensors are contiguous; else their element strides
+    (batch, head, row each) for the strided entry points, which need the head
+    dimension contiguous."""
     if all(t.is_contiguous() for t in ts):
         return None
     if any(t.dim() != 4 or (t.shape[3] > 1 and t.stride(3) != 1) for t in ts):
-        raise ValueError("q, k, v and out need a contiguous last (head) dimension")
+        raise ValueError("attention tensors need a contiguous last (head) dimension")
     out = []
     for t in ts:
         # a size-1 dimension's stride is arbitrary in torch: batch / head get
@@ -274,35 +285,46 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     q, k, v, o, dout: [B, H, S, d] fp16/bf16 device tensors (o and lse from
     ``forward`` on the same inputs, causal flag and scale); lse: [B, H, S]
     float32.  ``delta`` is a [B, H, S] float32 scratch buffer the call fills
-    with D_i = dout_i . o_i (allocated here if not given).  Asynchronous on
-    ``stream`` (default: the current stream).
+    with D_i = dout_i . o_i (allocated here if not given).  Tensors with a
+    contiguous last dimension but other strides (a [B, S, H, d] storage seen
+    through ``transpose(1, 2)``, slices of a packed QKV buffer) go through
+    fa_bwd_strided; gradients allocated here match q's layout.  Asynchronous
+    on ``stream`` (default: the current stream).
     """
     ts = (q, k, v, o, dout)
     if q.dim() != 4 or any(t.shape != q.shape for t in ts):
         raise ValueError("q, k, v, o, dout must share one [B, H, S, d] shape")
     if any(t.dtype != q.dtype for t in ts) or q.dtype not in _DTYPES:
         raise TypeError("q, k, v, o, dout must all be float16 or all bfloat16")
-    if not all(t.is_cuda and t.is_contiguous() for t in ts):
-        raise ValueError("q, k, v, o, dout must be contiguous device tensors")
+    if not all(t.is_cuda for t in ts):
+        raise ValueError("q, k, v, o, dout must be device tensors")
     B, H, S, d = q.shape
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
     if scale is None:
         scale = float(torch.tensor(d, dtype=torch.float32).rsqrt())
+    # empty_like keeps q's strides when q is dense in some permutation
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     if delta is None:
         delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor like q")
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor like q")
     if delta.shape != (B, H, S) or delta.dtype != torch.float32 or not delta.is_contiguous():
         raise ValueError("delta must be a contiguous float32 [B, H, S] tensor")
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, S, d, 1 if causal else 0,
-                scale, _DTYPES[q.dtype], s.cuda_stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
+    strides = _layout(q, k, v, o, dout, dq, dk, dv)
+    if strides is None:
+        st = fa_bwd(*ptrs, B, H, S, d, 1 if causal else 0, scale, _DTYPES[q.dtype], s.cuda_stream)
+        entry = "fa_bwd"
+    else:
+        st = fa_bwd_strided(*ptrs, B, H, S, d, strides, 1 if causal else 0, scale, _DTYPES[q.dtype],
+                            s.cuda_stream)
+        entry = "fa_bwd_strided"
     if st != FA_OK:
-        raise FaError(st, "fa_bwd")
+        raise FaError(st, entry)
     return dq, dk, dv

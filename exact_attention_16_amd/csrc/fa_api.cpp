@@ -110,15 +110,18 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
+// fa_bwd and fa_bwd_strided (strides != NULL: q, k, v, o, dout, dq, dk, dv
+// batch/head/row element strides).
 int validate_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                  void* dq, void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale,
-                 int dtype) {
+                 int dtype, const long long* strides = nullptr, bool strided = false) {
   if (B < 0 || H < 0 || S < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   if ((long long)B * H * S == 0) return FA_OK;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta || (strided && !strides))
+    return FA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
        (uintptr_t)dk | (uintptr_t)dv) & 15u)
     return FA_ERR_ALIGN;
@@ -127,12 +130,23 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   fa::BwdArgs a{};
   a.B = B; a.H = H; a.S = S; a.d = d;
   if (fa::bwd_grid_size(a) > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
-  const size_t nt = (size_t)B * H * S * d * 2;
+  // byte extents of q, k, v, o, dout, dq, dk, dv (dense, or from the strides)
+  size_t ext[8];
+  for (int t = 0; t < 8; ++t) {
+    Layout l = dense_layout(H, S, d);
+    if (strided) {
+      l = {strides[3 * t], strides[3 * t + 1], strides[3 * t + 2]};
+      const int st = check_layout(l, S, d);
+      if (st != FA_OK) return st;
+      if (t >= 5 && !injective(l, B, H, S, d)) return FA_ERR_STRIDE;  // dq, dk, dv
+    }
+    ext[t] = extent_bytes(l, B, H, S, d);
+  }
   const size_t nl = (size_t)B * H * S * 4;
   const void* ins[6] = {q, k, v, o, dout, lse};
-  const size_t in_bytes[6] = {nt, nt, nt, nt, nt, nl};
+  const size_t in_bytes[6] = {ext[0], ext[1], ext[2], ext[3], ext[4], nl};
   const void* outs[4] = {dq, dk, dv, delta};
-  const size_t out_bytes[4] = {nt, nt, nt, nl};
+  const size_t out_bytes[4] = {ext[5], ext[6], ext[7], nl};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return FA_ERR_ALIAS;
@@ -202,6 +216,24 @@ int decode(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(fa::launch_decode(a, plan, (hipStream_t)stream));
 }
 
+int backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+             void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale, int dtype,
+             void* stream, const long long* strides = nullptr, bool strided = false) {
+  const int st =
+      validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, strides, strided);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * S == 0) return FA_OK;
+  fa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.B = B; a.H = H; a.S = S; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.strides = strided ? strides : nullptr;
+  return hip_status(fa::launch_bwd(a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,17 +275,13 @@ int fa_fwd_decode_strided(const void* q, const void* k, const void* v, void* o, 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale, int dtype,
            void* stream) {
-  const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype);
-  if (st != FA_OK) return st;
-  if ((long long)B * H * S == 0) return FA_OK;
-  fa::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
-  a.B = B; a.H = H; a.S = S; a.d = d;
-  a.causal = causal != 0;
-  a.scale = scale;
-  a.dtype = dtype;
-  return hip_status(fa::launch_bwd(a, (hipStream_t)stream));
+  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, stream);
+}
+
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, float* delta, int B, int H, int S, int d, const long long* strides,
+                   int causal, float scale, int dtype, void* stream) {
+  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, stream, strides, true);
 }
 
 const char* fa_status_string(int status) {

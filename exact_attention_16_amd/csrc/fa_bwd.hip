@@ -60,7 +60,38 @@ struct BwdParams {
   int nblk;     // row blocks per head (query blocks for dq_kernel, key blocks for dkdv_kernel)
   float scale;
   float c;      // scale * log2(e)
+  // Strided layouts only: heads per batch entry, and per tensor (kQ .. kDV)
+  // the batch and head strides (elements) and the row stride (bytes).
+  int H;
+  long long sb[8], sh[8];
+  uint32_t rs[8];
 };
+
+enum { kQ, kK, kV, kO, kDO, kDQ, kDK, kDV };
+
+// One head of one tensor: base, bytes between rows and the byte range that
+// ends with the head's last row (rows past it read 0 / are dropped).
+struct View {
+  const char* base;
+  uint32_t rs;
+  uint32_t bytes;
+};
+
+template <int D, bool STRIDED>
+__device__ __forceinline__ View head_view(const BwdParams& p, const void* ptr, int t, int bh) {
+  View v;
+  if (STRIDED) {
+    const int b = bh / p.H, hh = bh - b * p.H;
+    v.base = (const char*)ptr + (b * p.sb[t] + hh * p.sh[t]) * 2;
+    v.rs = p.rs[t];
+    v.bytes = (uint32_t)(p.S - 1) * p.rs[t] + D * 2;
+  } else {
+    v.base = (const char*)ptr + (size_t)bh * p.S * D * 2;
+    v.rs = D * 2;
+    v.bytes = (uint32_t)p.S * D * 2;
+  }
+  return v;
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -82,19 +113,21 @@ struct Tile {
   static constexpr int LOADS = BYTES / (NW * 64 * 16);
   static_assert(LOADS * NW * 64 * 16 == BYTES, "tile must split evenly over lanes");
 
+  // rs: bytes between rows (ROW_BYTES for dense tensors); base: the tile's
+  // first row offset in bytes.
   static __device__ __forceinline__ void issue_a(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
-                                                 int lane) {
+                                                 int lane, uint32_t rs = ROW_BYTES) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int f = i * NW + wave;  // block (rb, kk)
       const int rb = f / KSTEPS, kk = f % KSTEPS;
-      const uint32_t off = base + (uint32_t)(rb * 32 + (lane & 31)) * ROW_BYTES + (kk * 2 + (lane >> 5)) * 16;
+      const uint32_t off = base + (uint32_t)(rb * 32 + (lane & 31)) * rs + (kk * 2 + (lane >> 5)) * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + f * 1024), 16, off, 0, 0, 0);
     }
   }
 
   static __device__ __forceinline__ void issue_t(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
-                                                 int lane) {
+                                                 int lane, uint32_t rs = ROW_BYTES) {
     const int x = lane >> 5;
     const int lp = lane & 31;
     const int vg = lp >> 3;
@@ -104,7 +137,7 @@ struct Tile {
     for (int i = 0; i < LOADS; ++i) {
       const int f = i * NW + wave;  // block ((rb * 2 + cc) * 2 + tt) * (DB / 2) + dp
       const int dp = f % (DB / 2), rest = f / (DB / 2);
-      const uint32_t off = base + (uint32_t)(rest * 8 + vrow) * ROW_BYTES + (dp * 64 + vcol) * 2;
+      const uint32_t off = base + (uint32_t)(rest * 8 + vrow) * rs + (dp * 64 + vcol) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + f * 1024), 16, off, 0, 0, 0);
     }
   }
@@ -131,11 +164,11 @@ struct Tile {
 // holds columns 16 kk + 8 (l/32) .. +8 of its row; rows past the range read 0.
 template <int D>
 __device__ __forceinline__ void load_row_frags(i16x8 (&f)[D / 16], const char* head, uint32_t head_bytes, int row,
-                                               int h) {
+                                               int h, uint32_t rs = D * 2) {
   const __amdgpu_buffer_rsrc_t r = rsrc(head, head_bytes);
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    const uint32_t off = (uint32_t)row * (D * 2) + (kk * 16 + h * 8) * 2;
+    const uint32_t off = (uint32_t)row * rs + (kk * 16 + h * 8) * 2;
     f[kk] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   }
 }
@@ -189,7 +222,7 @@ __device__ __forceinline__ void pack_c(const float (&e)[16], i16x8 (&out)[2]) {
 // `mul` as the lane's row of a row-major [rows x D] tensor in T.
 template <typename T, int D>
 __device__ __forceinline__ void store_row(const f32x16 (&acc)[D / 32], float mul, char* head, uint32_t head_bytes,
-                                          int row, int h) {
+                                          int row, int h, uint32_t rs = D * 2) {
   const __amdgpu_buffer_rsrc_t r = rsrc(head, head_bytes);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -199,7 +232,7 @@ __device__ __forceinline__ void store_row(const f32x16 (&acc)[D / 32], float mul
       w[0] = Elem<T>::pack(acc[db][4 * rg + 0] * mul, acc[db][4 * rg + 1] * mul);
       w[1] = Elem<T>::pack(acc[db][4 * rg + 2] * mul, acc[db][4 * rg + 3] * mul);
       const int col = db * 32 + 8 * rg + 4 * h;
-      __builtin_amdgcn_raw_buffer_store_b64(w, r, (uint32_t)row * (D * 2) + col * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, (uint32_t)row * rs + col * 2, 0, 0);
     }
 }
 
@@ -283,7 +316,7 @@ struct DqWave {
   }
 };
 
-template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN>
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN, bool STRIDED>
 __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   using W = DqWave<T, D, CAUSAL, TAIL, NW, BN>;
   using KT = typename W::KT;
@@ -307,20 +340,19 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   w.S = p.S;
   w.c = p.c;
 
-  const size_t head_elems = (size_t)bh * p.S * D;
-  const uint32_t head_bytes = (uint32_t)p.S * D * 2;
-  const char* kh = (const char*)p.k + head_elems * 2;
-  const char* vh = (const char*)p.v + head_elems * 2;
-  const __amdgpu_buffer_rsrc_t rk = rsrc(kh, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = rsrc(vh, head_bytes);
+  const View kv = head_view<D, STRIDED>(p, p.k, kK, bh), vv = head_view<D, STRIDED>(p, p.v, kV, bh);
+  const View qv = head_view<D, STRIDED>(p, p.q, kQ, bh), dov = head_view<D, STRIDED>(p, p.dout, kDO, bh);
+  const View ov = head_view<D, STRIDED>(p, p.o, kO, bh), dqv = head_view<D, STRIDED>(p, p.dq, kDQ, bh);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kv.base, kv.bytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vv.base, vv.bytes);
 
   // Q and dO rows of the lane's query; D_i = dO_i . O_i (each lane holds half
   // the columns, its partner lane l^32 the other half); LSE_i in log2 units.
-  load_row_frags<D>(w.qf, (const char*)p.q + head_elems * 2, head_bytes, w.myq, w.h);
-  load_row_frags<D>(w.dof, (const char*)p.dout + head_elems * 2, head_bytes, w.myq, w.h);
+  load_row_frags<D>(w.qf, qv.base, qv.bytes, w.myq, w.h, qv.rs);
+  load_row_frags<D>(w.dof, dov.base, dov.bytes, w.myq, w.h, dov.rs);
   {
     i16x8 of[W::KSTEPS];
-    load_row_frags<D>(of, (const char*)p.o + head_elems * 2, head_bytes, w.myq, w.h);
+    load_row_frags<D>(of, ov.base, ov.bytes, w.myq, w.h, ov.rs);
     float part = 0.f;
 #pragma unroll
     for (int kk = 0; kk < W::KSTEPS; ++kk) part = dot_pairs<T>(w.dof[kk], of[kk], part);
@@ -337,18 +369,18 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
 
   const int kv_end = CAUSAL ? min(p.S, q_lo + BM) : p.S;
   const int n = (kv_end + BN - 1) / BN;
-  const uint32_t tb = (uint32_t)BN * D * 2;
+  const uint32_t tk = (uint32_t)BN * kv.rs, tv = (uint32_t)BN * vv.rs;  // bytes per key tile
 
-  KT::issue_a(rk, 0, ka0, wave, w.lane);
-  KT::issue_a(rv, 0, va0, wave, w.lane);
-  KT::issue_t(rk, 0, kt0, wave, w.lane);
+  KT::issue_a(rk, 0, ka0, wave, w.lane, kv.rs);
+  KT::issue_a(rv, 0, va0, wave, w.lane, vv.rs);
+  KT::issue_t(rk, 0, kt0, wave, w.lane, kv.rs);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   barrier();
   for (int k = 0; k < n; k += 2) {
     if (k + 1 < n) {
-      KT::issue_a(rk, (k + 1) * tb, ka1, wave, w.lane);
-      KT::issue_a(rv, (k + 1) * tb, va1, wave, w.lane);
-      KT::issue_t(rk, (k + 1) * tb, kt1, wave, w.lane);
+      KT::issue_a(rk, (k + 1) * tk, ka1, wave, w.lane, kv.rs);
+      KT::issue_a(rv, (k + 1) * tv, va1, wave, w.lane, vv.rs);
+      KT::issue_t(rk, (k + 1) * tk, kt1, wave, w.lane, kv.rs);
     }
     if (w.active(k * BN)) {
       if (w.masked(k * BN)) w.template step<true>(ka0, va0, kt0, k * BN);
@@ -358,9 +390,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
     barrier();
     if (k + 1 >= n) break;
     if (k + 2 < n) {
-      KT::issue_a(rk, (k + 2) * tb, ka0, wave, w.lane);
-      KT::issue_a(rv, (k + 2) * tb, va0, wave, w.lane);
-      KT::issue_t(rk, (k + 2) * tb, kt0, wave, w.lane);
+      KT::issue_a(rk, (k + 2) * tk, ka0, wave, w.lane, kv.rs);
+      KT::issue_a(rv, (k + 2) * tv, va0, wave, w.lane, vv.rs);
+      KT::issue_t(rk, (k + 2) * tk, kt0, wave, w.lane, kv.rs);
     }
     if (w.active((k + 1) * BN)) {
       if (w.masked((k + 1) * BN)) w.template step<true>(ka1, va1, kt1, (k + 1) * BN);
@@ -369,7 +401,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     barrier();
   }
-  store_row<T, D>(w.dq, p.scale, (char*)p.dq + head_elems * 2, head_bytes, w.myq, w.h);
+  store_row<T, D>(w.dq, p.scale, (char*)dqv.base, dqv.bytes, w.myq, w.h, dqv.rs);
 }
 
 // ------------------------------------------------------------- dK/dV kernel
@@ -460,7 +492,7 @@ __device__ __forceinline__ void issue_stats(__amdgpu_buffer_rsrc_t rl, __amdgpu_
 template <int D>
 constexpr int dkdv_waves() { return D == 64 ? 8 : 4; }
 
-template <typename T, int D, bool CAUSAL, int NW, int BQ>
+template <typename T, int D, bool CAUSAL, int NW, int BQ, bool STRIDED>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParams p) {
   using W = DkvWave<T, D, CAUSAL, NW, BQ>;
   using QT = typename W::QT;
@@ -487,38 +519,39 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
   w.myk = w.kw + (w.lane & 31);
   w.c = p.c;
 
-  const size_t head_elems = (size_t)bh * p.S * D;
-  const uint32_t head_bytes = (uint32_t)p.S * D * 2;
-  load_row_frags<D>(w.kf, (const char*)p.k + head_elems * 2, head_bytes, w.myk, w.h);
-  load_row_frags<D>(w.vf, (const char*)p.v + head_elems * 2, head_bytes, w.myk, w.h);
+  const View kv = head_view<D, STRIDED>(p, p.k, kK, bh), vv = head_view<D, STRIDED>(p, p.v, kV, bh);
+  const View qv = head_view<D, STRIDED>(p, p.q, kQ, bh), dov = head_view<D, STRIDED>(p, p.dout, kDO, bh);
+  const View dkv = head_view<D, STRIDED>(p, p.dk, kDK, bh), dvv = head_view<D, STRIDED>(p, p.dv, kDV, bh);
+  load_row_frags<D>(w.kf, kv.base, kv.bytes, w.myk, w.h, kv.rs);
+  load_row_frags<D>(w.vf, vv.base, vv.bytes, w.myk, w.h, vv.rs);
 #pragma unroll
   for (int db = 0; db < W::DB; ++db) w.dk[db] = w.dv[db] = f32x16{};
 
-  const __amdgpu_buffer_rsrc_t rq = rsrc((const char*)p.q + head_elems * 2, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdo = rsrc((const char*)p.dout + head_elems * 2, head_bytes);
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qv.base, qv.bytes);
+  const __amdgpu_buffer_rsrc_t rdo = rsrc(dov.base, dov.bytes);
   const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (size_t)bh * p.S, (uint32_t)p.S * 4);
   const __amdgpu_buffer_rsrc_t rd = rsrc(p.delta + (size_t)bh * p.S, (uint32_t)p.S * 4);
 
   // query tiles t0 .. n-1 (causal: only queries >= the block's first key)
   const int t0 = CAUSAL ? k_lo / BQ : 0;
   const int n = (p.S + BQ - 1) / BQ;
-  const uint32_t tb = (uint32_t)BQ * D * 2;
+  const uint32_t tq = (uint32_t)BQ * qv.rs, tdo = (uint32_t)BQ * dov.rs;  // bytes per query tile
 
   if (t0 < n) {
-    QT::issue_a(rq, t0 * tb, qa0, wave, w.lane);
-    QT::issue_a(rdo, t0 * tb, da0, wave, w.lane);
-    QT::issue_t(rq, t0 * tb, qt0, wave, w.lane);
-    QT::issue_t(rdo, t0 * tb, dt0, wave, w.lane);
+    QT::issue_a(rq, t0 * tq, qa0, wave, w.lane, qv.rs);
+    QT::issue_a(rdo, t0 * tdo, da0, wave, w.lane, dov.rs);
+    QT::issue_t(rq, t0 * tq, qt0, wave, w.lane, qv.rs);
+    QT::issue_t(rdo, t0 * tdo, dt0, wave, w.lane, dov.rs);
     issue_stats<BQ>(rl, rd, t0 * BQ, st0, wave, w.lane);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   barrier();
   for (int t = t0; t < n; t += 2) {
     if (t + 1 < n) {
-      QT::issue_a(rq, (t + 1) * tb, qa1, wave, w.lane);
-      QT::issue_a(rdo, (t + 1) * tb, da1, wave, w.lane);
-      QT::issue_t(rq, (t + 1) * tb, qt1, wave, w.lane);
-      QT::issue_t(rdo, (t + 1) * tb, dt1, wave, w.lane);
+      QT::issue_a(rq, (t + 1) * tq, qa1, wave, w.lane, qv.rs);
+      QT::issue_a(rdo, (t + 1) * tdo, da1, wave, w.lane, dov.rs);
+      QT::issue_t(rq, (t + 1) * tq, qt1, wave, w.lane, qv.rs);
+      QT::issue_t(rdo, (t + 1) * tdo, dt1, wave, w.lane, dov.rs);
       issue_stats<BQ>(rl, rd, (t + 1) * BQ, st1, wave, w.lane);
     }
     if (w.active(t * BQ)) {
@@ -529,10 +562,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
     barrier();
     if (t + 1 >= n) break;
     if (t + 2 < n) {
-      QT::issue_a(rq, (t + 2) * tb, qa0, wave, w.lane);
-      QT::issue_a(rdo, (t + 2) * tb, da0, wave, w.lane);
-      QT::issue_t(rq, (t + 2) * tb, qt0, wave, w.lane);
-      QT::issue_t(rdo, (t + 2) * tb, dt0, wave, w.lane);
+      QT::issue_a(rq, (t + 2) * tq, qa0, wave, w.lane, qv.rs);
+      QT::issue_a(rdo, (t + 2) * tdo, da0, wave, w.lane, dov.rs);
+      QT::issue_t(rq, (t + 2) * tq, qt0, wave, w.lane, qv.rs);
+      QT::issue_t(rdo, (t + 2) * tdo, dt0, wave, w.lane, dov.rs);
       issue_stats<BQ>(rl, rd, (t + 2) * BQ, st0, wave, w.lane);
     }
     if (w.active((t + 1) * BQ)) {
@@ -542,8 +575,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     barrier();
   }
-  store_row<T, D>(w.dk, p.scale, (char*)p.dk + head_elems * 2, head_bytes, w.myk, w.h);
-  store_row<T, D>(w.dv, 1.0f, (char*)p.dv + head_elems * 2, head_bytes, w.myk, w.h);
+  store_row<T, D>(w.dk, p.scale, (char*)dkv.base, dkv.bytes, w.myk, w.h, dkv.rs);
+  store_row<T, D>(w.dv, 1.0f, (char*)dvv.base, dvv.bytes, w.myk, w.h, dvv.rs);
 }
 
 // ------------------------------------------------------------------ launch
@@ -554,7 +587,7 @@ constexpr int dq_key_tile() { return D == 64 ? 64 : 32; }
 template <int D>
 constexpr int dkdv_query_tile() { return D == 64 ? 64 : 32; }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool STRIDED>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   BwdParams p;
   p.q = a.q;
@@ -571,16 +604,23 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.S = a.S;
   p.scale = a.scale;
   p.c = a.scale * kLog2e;
+  p.H = a.H;
+  if (STRIDED)  // q, k, v, o, dout, dq, dk, dv: batch, head, row (elements)
+    for (int t = 0; t < 8; ++t) {
+      p.sb[t] = a.strides[3 * t];
+      p.sh[t] = a.strides[3 * t + 1];
+      p.rs[t] = (uint32_t)(a.strides[3 * t + 2] * 2);
+    }
 
   constexpr int BM = kDqWaves * 32;
   constexpr int BN = dq_key_tile<D>();
   p.nblk = (a.S + BM - 1) / BM;
   const bool tail = a.S % BN != 0;
   if (tail)
-    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, true, kDqWaves, BN>), dim3((unsigned)(p.nblk * p.BH)),
+    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, true, kDqWaves, BN, STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
                        dim3(kDqWaves * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, false, kDqWaves, BN>), dim3((unsigned)(p.nblk * p.BH)),
+    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, false, kDqWaves, BN, STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
                        dim3(kDqWaves * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -588,14 +628,19 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   constexpr int NW = dkdv_waves<D>();
   constexpr int BK = NW * 32;
   p.nblk = (a.S + BK - 1) / BK;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, NW, dkdv_query_tile<D>()>), dim3((unsigned)(p.nblk * p.BH)),
-                     dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, NW, dkdv_query_tile<D>(), STRIDED>),
+                     dim3((unsigned)(p.nblk * p.BH)), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename T, int D, bool STRIDED>
+hipError_t launch_bwd_s(const BwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch_bwd_t<T, D, true, STRIDED>(a, stream) : launch_bwd_t<T, D, false, STRIDED>(a, stream);
 }
 
 template <typename T, int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  return a.causal ? launch_bwd_t<T, D, true>(a, stream) : launch_bwd_t<T, D, false>(a, stream);
+  return a.strides ? launch_bwd_s<T, D, true>(a, stream) : launch_bwd_s<T, D, false>(a, stream);
 }
 
 template <typename T>

@@ -51,6 +51,9 @@ struct BwdArgs {
   bool causal;
   float scale;
   int dtype;  // fa_dtype
+  // NULL: dense tensors.  Else 24 element strides (host memory, read at
+  // launch): batch, head, row of q, k, v, o, dout, dq, dk, dv.
+  const long long* strides;
 };
 
 // Largest work-group count of the backward launches (for the host-side

@@ -241,6 +241,27 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int B, int H, int S, int d, int causal, float scale, int dtype,
            void* stream);
 
+/*
+ * fa_bwd_strided -- fa_bwd on strided tensors, e.g. q, k, v, o, dout and the
+ * gradients in the [B][S][H][d] layout, or slices of a packed QKV buffer.
+ *
+ *   strides  host array of 24 element strides: batch, head and row stride of
+ *            q, k, v, o, dout, dq, dk, dv in that order (each tensor's
+ *            element (b, h, i, c) is at ptr[b*sb + h*sh + i*rs + c]).  Each
+ *            tensor must satisfy fa_fwd_strided's requirements (strides >= 0
+ *            and multiples of 8, rs >= d, row offsets within 32 bits); dq, dk
+ *            and dv must also be one-to-one (FA_ERR_STRIDE), and the byte
+ *            ranges they span must not overlap an input, lse, delta or each
+ *            other (FA_ERR_ALIAS).  lse and delta stay dense [B][H][S].
+ * Results are bitwise those of fa_bwd on the same values in the dense
+ * layout.  Errors and behaviour otherwise as fa_bwd.
+ */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk,
+                   void* dv, float* delta, int B, int H, int S, int d,
+                   const long long* strides, int causal, float scale,
+                   int dtype, void* stream);
+
 /* Static English text for a status code; never NULL. */
 const char* fa_status_string(int status);
 

@@ -29,7 +29,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_strided",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_strided", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_strided",
                                    "fa_fwd_decode_workspace_size", "fa_fwd_kv", "fa_fwd_strided",
                                    "fa_last_hip_error", "fa_status_string", "fa_version"]
 
@@ -239,3 +239,62 @@ def test_decode_strided_validation(lib):
     assert fa.fa_fwd_decode_strided(*args, bad, 0, 0.125, fa.FA_DTYPE_BF16, WS, 1 << 20, None) == -11
     assert fa.fa_fwd_decode_strided(*args, st, 0, 0.125, fa.FA_DTYPE_BF16, 0, 0, None) == -10
     assert fa.fa_fwd_decode_strided(*args, None, 0, 0.125, fa.FA_DTYPE_BF16, WS, 1 << 20, None) == -1
+
+
+# fa_bwd_strided: dense-equivalent strides (B=1, H=2, S=64, d=64) for all eight tensors
+DENSE_BWD = D64 * 8
+
+
+def call_bwd_st(strides=None, **kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    st = strides if strides is not None else DENSE_BWD
+    return fa.fa_bwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                             a["delta"], a["B"], a["H"], a["S"], a["d"], st, a["causal"], a["scale"], a["dtype"],
+                             None)
+
+
+def bwd_stride(i, value):
+    st = list(DENSE_BWD)
+    st[i] = value
+    return st
+
+
+def test_backward_strided_empty_problem(lib):
+    assert call_bwd_st(B=0) == 0 and call_bwd_st(S=0, d=48) == -3
+
+
+# Every case fails validation, so nothing is launched on these fake addresses.
+@pytest.mark.parametrize("strides,kw,status", [
+    (bwd_stride(2, 32), {}, -11), (bwd_stride(14, 0), {}, -11),          # row stride < d (q, dout)
+    (bwd_stride(3, -8), {}, -11),                                         # negative stride (k)
+    (bwd_stride(7, 68), {}, -6), (bwd_stride(23, 100), {}, -6),           # not 16-byte rows (v, dv)
+    (bwd_stride(16, 64 * 32), {}, -11),   # dq's two heads overlap
+    (bwd_stride(19, 0), {}, -11),         # dk's two heads written to one place
+    (bwd_stride(22, 64 * 63), {}, -11),   # dv's heads interleave rows
+    (bwd_stride(5, 1 << 22), {}, -8),     # 32-bit row offsets exceeded
+    # o's heads may share storage (it is only read): the layout passes and the
+    # later alias check is what fails
+    (bwd_stride(10, 0), dict(dq=BQ_), -7),
+    (None, dict(dq=BQ_), -7),
+])
+def test_backward_strided_validation_errors(lib, strides, kw, status):
+    assert call_bwd_st(strides, **kw) == status, fa.fa_status_string(status)
+
+
+def test_backward_strided_null_and_alias(lib):
+    assert fa.fa_bwd_strided(BQ_, BK_, BV_, BO_, BL_, BDO, BDQ, BDK, BDV, BDL, 1, 2, 64, 64, None, 0, 0.125,
+                             fa.FA_DTYPE_BF16, None) == -1
+    # dk 20000 bytes before dv: the dense dk (16 KiB) fits, a padded one
+    # (row stride 128, 32640 bytes) reaches into dv
+    dk = BDV - 20000
+    padded = list(DENSE_BWD)
+    padded[18:21] = [2 * 64 * 128, 64 * 128, 128]
+    assert call_bwd_st(padded, dk=dk) == -7
+    # dq as the first and dk as the second half of each 128-element row of one
+    # buffer: disjoint elements but overlapping byte ranges, which validation
+    # rejects
+    inter = list(DENSE_BWD)
+    inter[15:18] = [2 * 64 * 128, 64 * 128, 128]
+    inter[18:21] = [2 * 64 * 128, 64 * 128, 128]
+    assert call_bwd_st(inter, dk=BDQ + 128) == -7

@@ -1,5 +1,5 @@
-"""GPU parity of the strided entry points (fa_fwd_strided, fa_fwd_decode_strided)
-through the C ABI.
+"""GPU parity of the strided entry points (fa_fwd_strided, fa_fwd_decode_strided,
+fa_bwd_strided) through the C ABI.
 
 The strided kernels do the dense kernels' arithmetic in the same order, only
 addressing rows through the caller's strides, so on the same values they must
@@ -130,3 +130,91 @@ def test_strided_binding_errors():
     with pytest.raises(fa.FaError) as e:
         fa.forward(q, q, q, out=overlapped)
     assert e.value.status == fa.FA_ERR_STRIDE
+
+
+def packed_qkv(q, k, v):
+    """q, k, v as slices of one [B, S, 3, H, d] buffer (a fused QKV
+    projection's output), each returned as a [B, H, S, d] view."""
+    B, H, S, d = q.shape
+    buf = torch.empty(B, S, 3, H, d, dtype=q.dtype, device=q.device)
+    for i, x in enumerate((q, k, v)):
+        buf[:, :, i] = x.transpose(1, 2)
+    return tuple(buf[:, :, i].transpose(1, 2) for i in range(3))
+
+
+def backward_inputs(B, H, S, d, dtype, seed):
+    q, k, v = (x.cuda() for x in make_inputs_kv(B, H, S, S, d, dtype, seed=seed))
+    g = torch.Generator().manual_seed(seed + 777_777)
+    do = torch.randn(B, H, S, d, generator=g).to(q.dtype).cuda()
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("layout", ["bshd", "padded", "packed"])
+@pytest.mark.parametrize("S", [1, 200, 777])
+def test_backward_strided_equals_dense(S, layout, d, causal):
+    """Gradients through fa_bwd_strided are bitwise those of fa_bwd; the
+    gradients allocated by the binding take q's layout."""
+    q, k, v, do = backward_inputs(2, 3, S, d, "bf16", seed=94_000 + S + d)
+    scale = default_scale(d)
+    label = f"strided bwd {layout} S={S} d={d} causal={causal}"
+    say(label)
+    o, lse = fa.forward(q, k, v, causal=causal, scale=scale)
+    ref = fa.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+    if layout == "packed":
+        qs, ks, vs = packed_qkv(q, k, v)
+        os_, dos = bshd(o), bshd(do)
+    else:
+        f = LAYOUTS[layout]
+        qs, ks, vs, os_, dos = f(q), f(k), f(v), f(o), f(do)
+    got = fa.backward(qs, ks, vs, os_, lse, dos, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    if layout == "bshd" and S > 1:
+        assert all(g.stride() == qs.stride() for g in got)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(g, r), f"{label}: {name} differs from the dense result"
+
+
+def test_backward_strided_oracle_and_untouched():
+    """Gradients written into [B, S, H, d] views of buffers with padded rows
+    and an extra head: they match the fp64 oracle and leave every other
+    element of the buffers untouched."""
+    B, H, S, d = 1, 2, 300, 64
+    q, k, v, do = backward_inputs(B, H, S, d, "fp16", seed=95_000)
+    scale = default_scale(d)
+    say("strided bwd gradient views")
+    o, lse = fa.forward(bshd(q), bshd(k), bshd(v), causal=True, scale=scale)
+    bufs = [torch.full((B, S, H + 1, d + 8), 4321.0, dtype=q.dtype, device="cuda") for _ in range(3)]
+    dq, dk, dv = (b[:, :, 1:, :d].transpose(1, 2) for b in bufs)
+    fa.backward(bshd(q), bshd(k), bshd(v), o, lse, bshd(do), causal=True, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    mask = torch.ones_like(bufs[0], dtype=torch.bool)
+    mask[:, :, 1:, :d] = False
+    for b in bufs:
+        assert (b[mask] == 4321.0).all().item()
+    ref = oracle.attention_backward(to64(q.cpu()), to64(k.cpu()), to64(v.cpu()), to64(do.cpu()), True, scale,
+                                    workers=8)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        g = g.float().cpu().double().numpy()
+        err, mag = float(np.max(np.abs(g - r))), float(np.max(np.abs(r)))
+        print(f"strided bwd {name}: max|err|={err:.3e} max|ref|={mag:.3e}")
+        assert err <= 2e-2 * mag + 1e-4
+
+
+def test_backward_strided_binding_errors():
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(1, 2, 8, dtype=torch.float32, device="cuda")
+    buf = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    shared = buf.as_strided((1, 2, 8, 64), (1024, 0, 64, 1))  # both heads' dk on one slab
+    with pytest.raises(fa.FaError) as e:
+        fa.backward(q, q, q, q, lse, q, dk=shared)
+    assert e.value.status == fa.FA_ERR_STRIDE
+    with pytest.raises(ValueError):  # head dimension not contiguous
+        fa.backward(q.transpose(2, 3).contiguous().transpose(2, 3), q, q, q, lse, q)
+    # gradients as slices of one packed buffer: their elements are disjoint but
+    # their byte ranges overlap, which the library rejects
+    dq, dk, dv = packed_qkv(q, q, q)
+    with pytest.raises(fa.FaError) as e:
+        fa.backward(q, q, q, q, lse, q, dq=dq, dk=dk, dv=dv)
+    assert e.value.status == -7
