@@ -194,13 +194,13 @@ hipError_t launch_dtype(const FwdArgs& a, hipStream_t stream) {
 using namespace detail;
 
 long long fwd_grid_size(const FwdArgs& a) {
-  if (a.d > 128) return fwd_wide_grid_size(a);
+  if (uses_in_order_kernel(a)) return fwd_wide_grid_size(a);
   const int BM = kWaves * 32;
   return (long long)((a.S + BM - 1) / BM) * a.B * a.H;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  if (a.d > 128) return launch_fwd_wide(a, stream);  // fa_fwd_wide.hip
+  if (uses_in_order_kernel(a)) return launch_fwd_wide(a, stream);  // fa_fwd_wide.hip
   // dtype 0 = fp16, 1 = bf16 (fa_dtype)
   return a.dtype == 1 ? launch_dtype<__bf16>(a, stream) : launch_dtype<_Float16>(a, stream);
 }

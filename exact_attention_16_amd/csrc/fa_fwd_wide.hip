@@ -1,4 +1,5 @@
-// gfx950 forward kernel for wide heads (d = 192 and 256).
+// gfx950 in-order forward kernel: wide heads (d = 192 and 256), and short
+// causal problems at d = 64 and 128.
 //
 // Same method and wavefront code as the d = 64 / 128 kernel in fa_fwd.hip
 // (tiled exact attention with an online softmax, IPLEX blog
@@ -16,6 +17,12 @@
 // softmax work does not, so at these widths the in-order schedule loses
 // little.  K/V tiles (64 keys) are double-buffered in four LDS objects and
 // the next tile's loads are issued before the current tile is computed.
+//
+// At d = 64 and 128 the same kernel runs short causal problems (the host's
+// uses_in_order_kernel), at four and two wavefronts per SIMD: with only a
+// few key tiles per query block, its 128-row blocks split the triangle of
+// causal work more evenly over the compute units than the ping-pong
+// kernel's 256-row blocks, which outweighs the lost overlap.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,8 +37,12 @@ namespace detail {
 constexpr int kWideWaves = 4;
 constexpr int kWideKeys = 64;
 
+// Wavefronts per SIMD the register budget is sized for.
+template <int D>
+constexpr int wide_waves_per_simd() { return D == 64 ? 4 : D == 128 ? 2 : 1; }
+
 template <typename T, int D, bool CAUSAL, bool TAIL, bool STRIDED>
-__global__ __launch_bounds__(kWideWaves * 64, 1) void fwd_wide_kernel(Params p) {
+__global__ __launch_bounds__(kWideWaves * 64, wide_waves_per_simd<D>()) void fwd_wide_kernel(Params p) {
   using W = FwdWave<T, D, CAUSAL, TAIL, kWideWaves, kWideKeys, STRIDED>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[W::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_lds1[W::TILE_BYTES];
@@ -134,8 +145,11 @@ hipError_t launch_wide_s(const FwdArgs& a, hipStream_t stream) {
   if (a.causal)
     return tail ? launch_wide_t<T, D, true, true, STRIDED>(a, stream)
                 : launch_wide_t<T, D, true, false, STRIDED>(a, stream);
-  return tail ? launch_wide_t<T, D, false, true, STRIDED>(a, stream)
-              : launch_wide_t<T, D, false, false, STRIDED>(a, stream);
+  if constexpr (D <= 128)  // only causal problems come here at these widths
+    return hipErrorInvalidValue;
+  else
+    return tail ? launch_wide_t<T, D, false, true, STRIDED>(a, stream)
+                : launch_wide_t<T, D, false, false, STRIDED>(a, stream);
 }
 
 template <typename T, int D>
@@ -145,7 +159,12 @@ hipError_t launch_wide_d(const FwdArgs& a, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_wide_dtype(const FwdArgs& a, hipStream_t stream) {
-  return a.d == 192 ? launch_wide_d<T, 192>(a, stream) : launch_wide_d<T, 256>(a, stream);
+  switch (a.d) {
+    case 64: return launch_wide_d<T, 64>(a, stream);
+    case 128: return launch_wide_d<T, 128>(a, stream);
+    case 192: return launch_wide_d<T, 192>(a, stream);
+    default: return launch_wide_d<T, 256>(a, stream);
+  }
 }
 
 }  // namespace detail

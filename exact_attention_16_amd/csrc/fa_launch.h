@@ -31,10 +31,19 @@ long long fwd_grid_size(const FwdArgs& a);
 // Enqueue the forward kernels on `stream`; returns the launch status.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
-// The same for head dimensions 192 and 256 (fa_fwd_wide.hip), used by the two
-// functions above.
+// The same for the in-order kernel (fa_fwd_wide.hip), used by the two
+// functions above for head dimensions 192 and 256 and for short causal
+// problems at 64 and 128 (uses_in_order_kernel).
 long long fwd_wide_grid_size(const FwdArgs& a);
 hipError_t launch_fwd_wide(const FwdArgs& a, hipStream_t stream);
+
+// Short causal problems run faster on the in-order kernel's 128-row blocks:
+// with few key tiles per block, finer blocks balance the triangular work
+// better than the ping-pong kernel's 256 rows (measured on the MI355X).
+inline bool uses_in_order_kernel(const FwdArgs& a) {
+  if (a.d > 128) return true;
+  return a.causal && a.Sk <= (a.d == 64 ? 2048 : 1024);
+}
 
 struct BwdArgs {
   const void* q;
