@@ -38,7 +38,7 @@ PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 40
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_fwd_wave.h", "fa_device.h")]
+                  for f in ("fa_fwd.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")]
 DECODE_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
                   for f in ("fa_decode.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_fa_fwd.md")
