@@ -80,7 +80,7 @@ def recorded_traffic(workload: str, record: str = TRAFFIC_RECORD, sources=None):
     return None
 
 
-def time_workload(w, steps: int, warmup: int):
+def time_workload(w, steps: int, warmup: int, per_launch: bool = False):
     import torch
 
     import exact_attention_16_amd as fa
@@ -105,9 +105,22 @@ def time_workload(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
+    launch_ms = None
+    if per_launch:
+        # The kernel's own launch duration: a second pass of K launches, each
+        # between its own pair of events on the launch stream, so the gaps
+        # between back-to-back launches (part of the step time above) are
+        # left out, as in rocprofv3's per-dispatch durations.
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            fa.forward(q, k, v, causal=w.causal, scale=scale, out=out, lse=lse, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        launch_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     ok = bool(torch.isfinite(lse).all().item())
     del q, k, v, out, lse
-    return dict(total_ms=total_ms, wall_s=wall, finite=ok)
+    return dict(total_ms=total_ms, wall_s=wall, finite=ok, launch_ms=launch_ms)
 
 
 def time_backward(w, steps: int, warmup: int):
@@ -266,12 +279,12 @@ def main():
 
     w = WORKLOADS_BY_NAME[args.workload]
     torch.cuda.synchronize()
-    r = time_workload(w, args.steps, args.warmup)
+    r = time_workload(w, args.steps, args.warmup, per_launch=True)
     torch.cuda.synchronize()
     ms = r["total_ms"] / args.steps
     f = flops(w)
     value = f / (ms * 1e-3) / 1e12
-    avg_launch_s = ms * 1e-3
+    avg_launch_s = r["launch_ms"] * 1e-3
     ai = f / algorithmic_bytes(w)
     bytes_pl = algorithmic_bytes(w)
     if ai < RIDGE:
@@ -287,6 +300,8 @@ def main():
     roof["flops"] = f
     roof["mfma_frac"] = value / PEAK_MFMA_TFLOPS
     roof["kernel"] = "fa::detail::fwd_kernel"
+    roof["launch_ms"] = r["launch_ms"]  # per-launch event pairs (the kernel's own duration)
+    roof["step_ms"] = ms                # bracketed back-to-back launches (gaps included)
 
     def time_list(workloads):
         out = []
