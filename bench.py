@@ -106,6 +106,7 @@ def time_workload(w, steps: int, warmup: int, per_launch: bool = False):
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     launch_ms = None
+    launch_stats = None
     if per_launch:
         # For reference only: a second pass of K launches, each between its
         # own pair of events on the launch stream (launches that do not run
@@ -116,10 +117,13 @@ def time_workload(w, steps: int, warmup: int, per_launch: bool = False):
             fa.forward(q, k, v, causal=w.causal, scale=scale, out=out, lse=lse, stream=stream)
             b.record(stream)
         torch.cuda.synchronize()
-        launch_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+        per = sorted(a.elapsed_time(b) for a, b in evs)
+        launch_ms = sum(per) / steps
+        launch_stats = {"min_ms": per[0], "median_ms": per[len(per) // 2],
+                        "p90_ms": per[min(len(per) - 1, int(0.9 * len(per)))]}
     ok = bool(torch.isfinite(lse).all().item())
     del q, k, v, out, lse
-    return dict(total_ms=total_ms, wall_s=wall, finite=ok, launch_ms=launch_ms)
+    return dict(total_ms=total_ms, wall_s=wall, finite=ok, launch_ms=launch_ms, launch_stats=launch_stats)
 
 
 def time_backward(w, steps: int, warmup: int):
@@ -301,6 +305,7 @@ def main():
     roof["kernel"] = "fa::detail::fwd_kernel"
     roof["launch_ms"] = ms                          # the timed back-to-back launches
     roof["isolated_launch_ms"] = r["launch_ms"]     # the same kernel between per-launch event pairs
+    roof["isolated_launch_stats"] = r["launch_stats"]
 
     def time_list(workloads):
         out = []
