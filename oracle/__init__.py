@@ -16,6 +16,10 @@ from .gradient import (  # noqa: F401
     attention_backward_head,
     backward_samples,
 )
+from .gradient_kv import (  # noqa: F401
+    attention_backward_kv,
+    attention_backward_kv_head,
+)
 from .kv import (  # noqa: F401
     allowed_keys_kv,
     attention_kv,
