@@ -3,7 +3,8 @@
 ``forward(q, k, v, causal, scale) -> (o, lse)`` (k, v may hold a different
 number of rows than q), ``decode(q, k, v, causal, scale) -> (o, lse)`` (the
 same split over the keys, for a few queries over many keys) and
-``backward(q, k, v, o, lse, dout, causal, scale) -> (dq, dk, dv)`` run the HIP
+``backward(q, k, v, o, lse, dout, causal, scale) -> (dq, dk, dv)`` (also with
+separate lengths and strided layouts) run the HIP
 kernels of ``libfa.so`` through its C ABI (include/fa.h).  The library is
 loaded on first use and its absence is an error.
 """
@@ -17,6 +18,7 @@ from .binding import (  # noqa: F401
     backward,
     decode,
     fa_bwd,
+    fa_bwd_kv,
     fa_bwd_strided,
     fa_fwd,
     fa_fwd_decode,

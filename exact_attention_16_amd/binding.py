@@ -59,7 +59,9 @@ def load_library() -> ctypes.CDLL:
             lib.fa_fwd_decode_workspace_size.restype = ctypes.c_size_t
             lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
             lib.fa_bwd.restype = i
-            lib.fa_bwd_strided.argtypes = [vp] * 10 + [i, i, i, i, vp, i, f, i, vp]
+            lib.fa_bwd_kv.argtypes = [vp] * 10 + [i, i, i, i, i, i, f, i, vp]
+            lib.fa_bwd_kv.restype = i
+            lib.fa_bwd_strided.argtypes = [vp] * 10 + [i, i, i, i, i, vp, i, f, i, vp]
             lib.fa_bwd_strided.restype = i
             lib.fa_status_string.argtypes = [i]
             lib.fa_status_string.restype = ctypes.c_char_p
@@ -137,13 +139,19 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, 
                                       int(causal), float(scale), int(dtype), stream))
 
 
-def fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, strides, causal, scale, dtype,
+def fa_bwd_kv(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Sq, Sk, d, causal, scale, dtype, stream) -> int:
+    """The C entry point with plain integers as pointers; returns the status."""
+    return int(load_library().fa_bwd_kv(q, k, v, o, lse, dout, dq, dk, dv, delta, int(B), int(H), int(Sq), int(Sk),
+                                         int(d), int(causal), float(scale), int(dtype), stream))
+
+
+def fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Sq, Sk, d, strides, causal, scale, dtype,
                    stream) -> int:
     """The C entry point; ``strides`` is a sequence of 24 element strides (q, k,
     v, o, dout, dq, dk, dv: batch, head, row) or None; returns the status."""
     arg = _strides_arg(strides)
-    return int(load_library().fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, delta, int(B), int(H), int(S),
-                                              int(d), arg[0] if arg else None, int(causal), float(scale),
+    return int(load_library().fa_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, delta, int(B), int(H), int(Sq),
+                                              int(Sk), int(d), arg[0] if arg else None, int(causal), float(scale),
                                               int(dtype), stream))
 
 
@@ -282,49 +290,55 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
              delta: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
     """Gradients (dq, dk, dv) of exact attention for the upstream gradient dout.
 
-    q, k, v, o, dout: [B, H, S, d] fp16/bf16 device tensors (o and lse from
-    ``forward`` on the same inputs, causal flag and scale); lse: [B, H, S]
-    float32.  ``delta`` is a [B, H, S] float32 scratch buffer the call fills
-    with D_i = dout_i . o_i (allocated here if not given).  Tensors with a
-    contiguous last dimension but other strides (a [B, S, H, d] storage seen
-    through ``transpose(1, 2)``, slices of a packed QKV buffer) go through
-    fa_bwd_strided; gradients allocated here match q's layout.  Asynchronous
-    on ``stream`` (default: the current stream).
+    q, o, dout: [B, H, Sq, d] and k, v: [B, H, Sk, d] fp16/bf16 device tensors
+    (o and lse from ``forward`` on the same inputs, causal flag and scale;
+    with Sq != Sk the causal mask is aligned to the end, as in ``forward``);
+    lse: [B, H, Sq] float32.  ``delta`` is a [B, H, Sq] float32 scratch
+    buffer the call fills with D_i = dout_i . o_i (allocated here if not
+    given).  Square problems go through fa_bwd, others through fa_bwd_kv;
+    tensors with a contiguous last dimension but other strides (a
+    [B, S, H, d] storage seen through ``transpose(1, 2)``, slices of a packed
+    QKV buffer) through fa_bwd_strided.  Gradients allocated here match the
+    layout of q (dq) and k (dk, dv).  Asynchronous on ``stream`` (default:
+    the current stream).
     """
     ts = (q, k, v, o, dout)
-    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
-        raise ValueError("q, k, v, o, dout must share one [B, H, S, d] shape")
+    if q.dim() != 4 or any(t.dim() != 4 for t in ts):
+        raise ValueError("q, k, v, o, dout must be 4-d [B, H, S, d] tensors")
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    if o.shape != q.shape or dout.shape != q.shape or k.shape != (B, H, Sk, d) or v.shape != k.shape:
+        raise ValueError("q, o, dout must be [B, H, Sq, d] and k, v [B, H, Sk, d]")
     if any(t.dtype != q.dtype for t in ts) or q.dtype not in _DTYPES:
         raise TypeError("q, k, v, o, dout must all be float16 or all bfloat16")
     if not all(t.is_cuda for t in ts):
         raise ValueError("q, k, v, o, dout must be device tensors")
-    B, H, S, d = q.shape
-    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
     if scale is None:
         scale = float(torch.tensor(d, dtype=torch.float32).rsqrt())
-    # empty_like keeps q's strides when q is dense in some permutation
+    # empty_like keeps the source's strides when it is dense in some permutation
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
     if delta is None:
-        delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor like q")
-    if delta.shape != (B, H, S) or delta.dtype != torch.float32 or not delta.is_contiguous():
-        raise ValueError("delta must be a contiguous float32 [B, H, S] tensor")
+        delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t.shape != like.shape or t.dtype != q.dtype or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor shaped like {'q' if like is q else 'k'}")
+    if delta.shape != (B, H, Sq) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 [B, H, Sq] tensor")
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
     strides = _layout(q, k, v, o, dout, dq, dk, dv)
-    if strides is None:
-        st = fa_bwd(*ptrs, B, H, S, d, 1 if causal else 0, scale, _DTYPES[q.dtype], s.cuda_stream)
-        entry = "fa_bwd"
+    c, dt = 1 if causal else 0, _DTYPES[q.dtype]
+    if strides is not None:
+        st, entry = fa_bwd_strided(*ptrs, B, H, Sq, Sk, d, strides, c, scale, dt, s.cuda_stream), "fa_bwd_strided"
+    elif Sq == Sk:
+        st, entry = fa_bwd(*ptrs, B, H, Sq, d, c, scale, dt, s.cuda_stream), "fa_bwd"
     else:
-        st = fa_bwd_strided(*ptrs, B, H, S, d, strides, 1 if causal else 0, scale, _DTYPES[q.dtype],
-                            s.cuda_stream)
-        entry = "fa_bwd_strided"
+        st, entry = fa_bwd_kv(*ptrs, B, H, Sq, Sk, d, c, scale, dt, s.cuda_stream), "fa_bwd_kv"
     if st != FA_OK:
         raise FaError(st, entry)
     return dq, dk, dv

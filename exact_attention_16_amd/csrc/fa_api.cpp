@@ -18,6 +18,7 @@ thread_local char g_last_hip_error[256] = "";
 bool forward_head_dim(int d) { return d == 64 || d == 128 || d == 192 || d == 256; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (na == 0 || nb == 0) return false;  // an empty range overlaps nothing
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
 }
@@ -110,39 +111,52 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
-// fa_bwd and fa_bwd_strided (strides != NULL: q, k, v, o, dout, dq, dk, dv
-// batch/head/row element strides).
+// fa_bwd, fa_bwd_kv and fa_bwd_strided.  q, o, dout, dq, lse and delta hold
+// Sq rows per head, k, v, dk and dv Sk rows; strides != NULL: q, k, v, o,
+// dout, dq, dk, dv batch/head/row element strides.  square: fa_bwd's
+// contract (Sq = Sk = S; B*H*S == 0 is a no-op).  Otherwise a side with no
+// rows is not touched, so its pointers may be NULL: with Sq = 0 the call
+// writes dk = dv = 0, with Sk = 0 it writes dq = 0 and delta.
 int validate_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                 void* dq, void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale,
-                 int dtype, const long long* strides = nullptr, bool strided = false) {
-  if (B < 0 || H < 0 || S < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
+                 void* dq, void* dk, void* dv, float* delta, int B, int H, int Sq, int Sk, int d, int causal,
+                 float scale, int dtype, const long long* strides = nullptr, bool strided = false,
+                 bool square = false) {
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
-  if ((long long)B * H * S == 0) return FA_OK;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta || (strided && !strides))
+  if ((long long)B * H == 0 || (square ? Sq == 0 : (Sq == 0 && Sk == 0))) return FA_OK;
+  const bool qs = Sq > 0, ks = Sk > 0;  // which sides are touched
+  if ((qs && (!q || !o || !lse || !dout || !dq || !delta)) || (ks && (!k || !v || !dk || !dv)) ||
+      (strided && !strides))
     return FA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
        (uintptr_t)dk | (uintptr_t)dv) & 15u)
     return FA_ERR_ALIGN;
   if (((uintptr_t)lse | (uintptr_t)delta) & 3u) return FA_ERR_ALIGN;
-  if ((long long)S * d >= (1LL << 30)) return FA_ERR_TOO_LARGE;
+  if ((long long)Sq * d >= (1LL << 30) || (long long)Sk * d >= (1LL << 30)) return FA_ERR_TOO_LARGE;
   fa::BwdArgs a{};
-  a.B = B; a.H = H; a.S = S; a.d = d;
+  a.B = B; a.H = H; a.S = Sq; a.Sk = Sk; a.d = d;
   if (fa::bwd_grid_size(a) > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
   // byte extents of q, k, v, o, dout, dq, dk, dv (dense, or from the strides)
   size_t ext[8];
   for (int t = 0; t < 8; ++t) {
-    Layout l = dense_layout(H, S, d);
+    const bool key_side = t == 1 || t == 2 || t == 6 || t == 7;  // k, v, dk, dv
+    const int rows = key_side ? Sk : Sq;
+    if (rows == 0) {
+      ext[t] = 0;
+      continue;
+    }
+    Layout l = dense_layout(H, rows, d);
     if (strided) {
       l = {strides[3 * t], strides[3 * t + 1], strides[3 * t + 2]};
-      const int st = check_layout(l, S, d);
+      const int st = check_layout(l, rows, d);
       if (st != FA_OK) return st;
-      if (t >= 5 && !injective(l, B, H, S, d)) return FA_ERR_STRIDE;  // dq, dk, dv
+      if (t >= 5 && !injective(l, B, H, rows, d)) return FA_ERR_STRIDE;  // dq, dk, dv
     }
-    ext[t] = extent_bytes(l, B, H, S, d);
+    ext[t] = extent_bytes(l, B, H, rows, d);
   }
-  const size_t nl = (size_t)B * H * S * 4;
+  const size_t nl = (size_t)B * H * Sq * 4;
   const void* ins[6] = {q, k, v, o, dout, lse};
   const size_t in_bytes[6] = {ext[0], ext[1], ext[2], ext[3], ext[4], nl};
   const void* outs[4] = {dq, dk, dv, delta};
@@ -217,16 +231,16 @@ int decode(const void* q, const void* k, const void* v, void* o, float* lse, int
 }
 
 int backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
-             void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale, int dtype,
-             void* stream, const long long* strides = nullptr, bool strided = false) {
-  const int st =
-      validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, strides, strided);
+             void* dk, void* dv, float* delta, int B, int H, int Sq, int Sk, int d, int causal, float scale,
+             int dtype, void* stream, const long long* strides, bool strided, bool square) {
+  const int st = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Sq, Sk, d, causal, scale, dtype,
+                              strides, strided, square);
   if (st != FA_OK) return st;
-  if ((long long)B * H * S == 0) return FA_OK;
+  if ((long long)B * H == 0 || (Sq == 0 && Sk == 0) || (square && Sq == 0)) return FA_OK;
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
-  a.B = B; a.H = H; a.S = S; a.d = d;
+  a.B = B; a.H = H; a.S = Sq; a.Sk = Sk; a.d = d;
   a.causal = causal != 0;
   a.scale = scale;
   a.dtype = dtype;
@@ -275,13 +289,22 @@ int fa_fwd_decode_strided(const void* q, const void* k, const void* v, void* o, 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, float* delta, int B, int H, int S, int d, int causal, float scale, int dtype,
            void* stream) {
-  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, stream);
+  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, S, d, causal, scale, dtype, stream, nullptr,
+                  false, true);
+}
+
+int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, float* delta, int B, int H, int Sq, int Sk, int d, int causal,
+              float scale, int dtype, void* stream) {
+  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Sq, Sk, d, causal, scale, dtype, stream, nullptr,
+                  false, false);
 }
 
 int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                   void* dq, void* dk, void* dv, float* delta, int B, int H, int S, int d, const long long* strides,
-                   int causal, float scale, int dtype, void* stream) {
-  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, S, d, causal, scale, dtype, stream, strides, true);
+                   void* dq, void* dk, void* dv, float* delta, int B, int H, int Sq, int Sk, int d,
+                   const long long* strides, int causal, float scale, int dtype, void* stream) {
+  return backward(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Sq, Sk, d, causal, scale, dtype, stream, strides,
+                  true, false);
 }
 
 const char* fa_status_string(int status) {

@@ -56,7 +56,9 @@ struct BwdParams {
   void* dv;
   float* delta;
   int BH;
-  int S;
+  int S;        // query rows per head (q, o, dout, dq, lse, delta)
+  int Sk;       // key rows per head (k, v, dk, dv)
+  int shift;    // causal offset: key j is kept for query row i iff j <= i + shift (Sk - S)
   int nblk;     // row blocks per head (query blocks for dq_kernel, key blocks for dkdv_kernel)
   float scale;
   float c;      // scale * log2(e)
@@ -79,16 +81,17 @@ struct View {
 
 template <int D, bool STRIDED>
 __device__ __forceinline__ View head_view(const BwdParams& p, const void* ptr, int t, int bh) {
+  const int rows = (t == kK || t == kV || t == kDK || t == kDV) ? p.Sk : p.S;
   View v;
   if (STRIDED) {
     const int b = bh / p.H, hh = bh - b * p.H;
     v.base = (const char*)ptr + (b * p.sb[t] + hh * p.sh[t]) * 2;
     v.rs = p.rs[t];
-    v.bytes = (uint32_t)(p.S - 1) * p.rs[t] + D * 2;
+    v.bytes = rows > 0 ? (uint32_t)(rows - 1) * p.rs[t] + D * 2 : 0u;
   } else {
-    v.base = (const char*)ptr + (size_t)bh * p.S * D * 2;
+    v.base = (const char*)ptr + (size_t)bh * rows * D * 2;
     v.rs = D * 2;
-    v.bytes = (uint32_t)p.S * D * 2;
+    v.bytes = (uint32_t)rows * D * 2;
   }
   return v;
 }
@@ -268,14 +271,14 @@ struct DqWave {
   static constexpr int DB = D / 32;
   static constexpr int SB = BN / 32;
 
-  int lane, h, qw, myq, S;
+  int lane, h, qw, myq, Sk, shift;
   float c, lse2, dl;
   i16x8 qf[KSTEPS], dof[KSTEPS];
   f32x16 dq[DB];
 
-  __device__ __forceinline__ bool active(int k0) const { return !(CAUSAL && k0 > qw + 31); }
+  __device__ __forceinline__ bool active(int k0) const { return !(CAUSAL && k0 > qw + 31 + shift); }
   __device__ __forceinline__ bool masked(int k0) const {
-    return (CAUSAL && k0 + BN - 1 > qw) || (TAIL && k0 + BN > S);
+    return (CAUSAL && k0 + BN - 1 > qw + shift) || (TAIL && k0 + BN > Sk);
   }
 
   // One key tile: kA = K (A layout), vA = V (A layout), kT = K (T layout).
@@ -301,7 +304,9 @@ struct DqWave {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], c, -lse2));
         if (MASKED) {
           const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          p = (key < S && (!CAUSAL || key <= myq)) ? p : 0.f;
+          // a select, not a product: a row that keeps no key has LSE = -inf
+          // and p = +inf here
+          p = (key < Sk && (!CAUSAL || key <= myq + shift)) ? p : 0.f;
         }
         e[r] = p * (dp[sb][r] - dl);
       }
@@ -337,7 +342,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   const int q_lo = qb * BM;
   w.qw = q_lo + 32 * wave;
   w.myq = w.qw + (w.lane & 31);
-  w.S = p.S;
+  w.Sk = p.Sk;
+  w.shift = p.shift;
   w.c = p.c;
 
   const View kv = head_view<D, STRIDED>(p, p.k, kK, bh), vv = head_view<D, STRIDED>(p, p.v, kV, bh);
@@ -367,13 +373,16 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < W::DB; ++db) w.dq[db] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(p.S, q_lo + BM) : p.S;
-  const int n = (kv_end + BN - 1) / BN;
+  // keys this work-group visits (causal: up to its last row's position)
+  const int kv_end = CAUSAL ? min(p.Sk, q_lo + BM + p.shift) : p.Sk;
+  const int n = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
   const uint32_t tk = (uint32_t)BN * kv.rs, tv = (uint32_t)BN * vv.rs;  // bytes per key tile
 
-  KT::issue_a(rk, 0, ka0, wave, w.lane, kv.rs);
-  KT::issue_a(rv, 0, va0, wave, w.lane, vv.rs);
-  KT::issue_t(rk, 0, kt0, wave, w.lane, kv.rs);
+  if (n > 0) {
+    KT::issue_a(rk, 0, ka0, wave, w.lane, kv.rs);
+    KT::issue_a(rv, 0, va0, wave, w.lane, vv.rs);
+    KT::issue_t(rk, 0, kt0, wave, w.lane, kv.rs);
+  }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   barrier();
   for (int k = 0; k < n; k += 2) {
@@ -417,13 +426,13 @@ struct DkvWave {
   static constexpr int DB = D / 32;
   static constexpr int QB = BQ / 32;
 
-  int lane, h, kw, myk;
+  int lane, h, kw, myk, shift;
   float c;
   i16x8 kf[KSTEPS], vf[KSTEPS];
   f32x16 dk[DB], dv[DB];
 
-  __device__ __forceinline__ bool active(int q0) const { return !(CAUSAL && q0 + BQ - 1 < kw); }
-  __device__ __forceinline__ bool masked(int q0) const { return CAUSAL && q0 < kw + 31; }
+  __device__ __forceinline__ bool active(int q0) const { return !(CAUSAL && q0 + BQ - 1 + shift < kw); }
+  __device__ __forceinline__ bool masked(int q0) const { return CAUSAL && q0 + shift < kw + 31; }
 
   // One query tile: qA, dA = Q, dO (A layout); qT, dT = Q, dO (T layout);
   // st = the tile's LSE (floats 0..BQ-1) and D (floats kStatFloats..).
@@ -457,7 +466,8 @@ struct DkvWave {
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * j + t;
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c, -lv[t] * kLog2e));
-          if (MASKED) p = (q0 + qi + t >= myk) ? p : 0.f;
+          // a select: a row that keeps no key has LSE = -inf and p = +inf
+          if (MASKED) p = (q0 + qi + t + shift >= myk) ? p : 0.f;
           pe[r] = p;
           de[r] = p * (dp[qb][r] - dvv[t]);
         }
@@ -518,6 +528,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
   w.kw = k_lo + 32 * wave;
   w.myk = w.kw + (w.lane & 31);
   w.c = p.c;
+  w.shift = p.shift;
 
   const View kv = head_view<D, STRIDED>(p, p.k, kK, bh), vv = head_view<D, STRIDED>(p, p.v, kV, bh);
   const View qv = head_view<D, STRIDED>(p, p.q, kQ, bh), dov = head_view<D, STRIDED>(p, p.dout, kDO, bh);
@@ -532,8 +543,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
   const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (size_t)bh * p.S, (uint32_t)p.S * 4);
   const __amdgpu_buffer_rsrc_t rd = rsrc(p.delta + (size_t)bh * p.S, (uint32_t)p.S * 4);
 
-  // query tiles t0 .. n-1 (causal: only queries >= the block's first key)
-  const int t0 = CAUSAL ? k_lo / BQ : 0;
+  // query tiles t0 .. n-1 (causal: only queries whose position i + shift
+  // reaches the block's first key)
+  const int t0 = CAUSAL ? max(0, k_lo - p.shift) / BQ : 0;
   const int n = (p.S + BQ - 1) / BQ;
   const uint32_t tq = (uint32_t)BQ * qv.rs, tdo = (uint32_t)BQ * dov.rs;  // bytes per query tile
 
@@ -602,6 +614,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.delta = a.delta;
   p.BH = a.B * a.H;
   p.S = a.S;
+  p.Sk = a.Sk;
+  p.shift = a.causal ? a.Sk - a.S : 0;
   p.scale = a.scale;
   p.c = a.scale * kLog2e;
   p.H = a.H;
@@ -614,20 +628,25 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
   constexpr int BM = kDqWaves * 32;
   constexpr int BN = dq_key_tile<D>();
+  // no query rows: no dq_kernel (nothing to write); no key rows: no
+  // dkdv_kernel (the dq_kernel then writes dq = 0 and delta)
   p.nblk = (a.S + BM - 1) / BM;
-  const bool tail = a.S % BN != 0;
-  if (tail)
-    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, true, kDqWaves, BN, STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
-                       dim3(kDqWaves * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, false, kDqWaves, BN, STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
-                       dim3(kDqWaves * 64), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool tail = a.Sk % BN != 0;
+  if (p.nblk > 0) {
+    if (tail)
+      hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, true, kDqWaves, BN, STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
+                         dim3(kDqWaves * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, false, kDqWaves, BN, STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
+                         dim3(kDqWaves * 64), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   constexpr int NW = dkdv_waves<D>();
   constexpr int BK = NW * 32;
-  p.nblk = (a.S + BK - 1) / BK;
+  p.nblk = (a.Sk + BK - 1) / BK;
+  if (p.nblk == 0) return hipSuccess;
   hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, NW, dkdv_query_tile<D>(), STRIDED>),
                      dim3((unsigned)(p.nblk * p.BH)), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
@@ -654,7 +673,7 @@ long long bwd_grid_size(const BwdArgs& a) {
   const long long bh = (long long)a.B * a.H;
   const long long dq = (long long)((a.S + bwd::kDqWaves * 32 - 1) / (bwd::kDqWaves * 32)) * bh;
   const int bk = (a.d == 64 ? bwd::dkdv_waves<64>() : bwd::dkdv_waves<128>()) * 32;
-  const long long dkdv = (long long)((a.S + bk - 1) / bk) * bh;
+  const long long dkdv = (long long)((a.Sk + bk - 1) / bk) * bh;
   return dq > dkdv ? dq : dkdv;
 }
 

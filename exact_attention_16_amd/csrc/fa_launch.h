@@ -57,6 +57,7 @@ struct BwdArgs {
   void* dv;
   float* delta;
   int B, H, S, d;
+  int Sk;       // key rows per head (= S for self-attention)
   bool causal;
   float scale;
   int dtype;  // fa_dtype

@@ -242,8 +242,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* stream);
 
 /*
- * fa_bwd_strided -- fa_bwd on strided tensors, e.g. q, k, v, o, dout and the
- * gradients in the [B][S][H][d] layout, or slices of a packed QKV buffer.
+ * fa_bwd_kv -- fa_bwd with separate query and key lengths: the gradients of
+ * fa_fwd_kv (same end-aligned causal mask: key j is kept for query row i iff
+ * j <= i + Sk - Sq).
+ *
+ *   q, o, dout, dq  [B][H][Sq][d];  lse, delta  [B][H][Sq] fp32;
+ *   k, v, dk, dv    [B][H][Sk][d].
+ *
+ * A query row that keeps no key (causal with Sq > Sk, rows i < Sq - Sk; its
+ * forward output is the constant 0 and its LSE -inf) gets dq = 0 and adds
+ * nothing to dk and dv.  With Sq = 0 the call writes dk = dv = 0 and the
+ * query-side pointers may be NULL; with Sk = 0 it writes dq = 0 and delta
+ * and the key-side pointers may be NULL; B*H == 0 or Sq = Sk = 0 is a no-op.
+ * With Sq = Sk the results are bitwise those of fa_bwd.  Errors and
+ * behaviour otherwise as fa_bwd.
+ */
+int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o,
+              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+              float* delta, int B, int H, int Sq, int Sk, int d, int causal,
+              float scale, int dtype, void* stream);
+
+/*
+ * fa_bwd_strided -- fa_bwd_kv on strided tensors, e.g. q, k, v, o, dout and
+ * the gradients in the [B][S][H][d] layout, or slices of a packed QKV buffer.
  *
  *   strides  host array of 24 element strides: batch, head and row stride of
  *            q, k, v, o, dout, dq, dk, dv in that order (each tensor's
@@ -252,13 +273,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  *            and multiples of 8, rs >= d, row offsets within 32 bits); dq, dk
  *            and dv must also be one-to-one (FA_ERR_STRIDE), and the byte
  *            ranges they span must not overlap an input, lse, delta or each
- *            other (FA_ERR_ALIAS).  lse and delta stay dense [B][H][S].
- * Results are bitwise those of fa_bwd on the same values in the dense
- * layout.  Errors and behaviour otherwise as fa_bwd.
+ *            other (FA_ERR_ALIAS).  lse and delta stay dense [B][H][Sq].
+ * Results are bitwise those of fa_bwd_kv on the same values in the dense
+ * layout.  Errors and behaviour otherwise as fa_bwd_kv.
  */
 int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dout, void* dq, void* dk,
-                   void* dv, float* delta, int B, int H, int S, int d,
+                   void* dv, float* delta, int B, int H, int Sq, int Sk, int d,
                    const long long* strides, int causal, float scale,
                    int dtype, void* stream);
 

@@ -29,7 +29,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_strided", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_strided",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_kv", "fa_bwd_strided", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_strided",
                                    "fa_fwd_decode_workspace_size", "fa_fwd_kv", "fa_fwd_strided",
                                    "fa_last_hip_error", "fa_status_string", "fa_version"]
 
@@ -250,8 +250,8 @@ def call_bwd_st(strides=None, **kw):
     a.update(kw)
     st = strides if strides is not None else DENSE_BWD
     return fa.fa_bwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
-                             a["delta"], a["B"], a["H"], a["S"], a["d"], st, a["causal"], a["scale"], a["dtype"],
-                             None)
+                             a["delta"], a["B"], a["H"], a["S"], a["S"], a["d"], st, a["causal"], a["scale"],
+                             a["dtype"], None)
 
 
 def bwd_stride(i, value):
@@ -283,7 +283,7 @@ def test_backward_strided_validation_errors(lib, strides, kw, status):
 
 
 def test_backward_strided_null_and_alias(lib):
-    assert fa.fa_bwd_strided(BQ_, BK_, BV_, BO_, BL_, BDO, BDQ, BDK, BDV, BDL, 1, 2, 64, 64, None, 0, 0.125,
+    assert fa.fa_bwd_strided(BQ_, BK_, BV_, BO_, BL_, BDO, BDQ, BDK, BDV, BDL, 1, 2, 64, 64, 64, None, 0, 0.125,
                              fa.FA_DTYPE_BF16, None) == -1
     # dk 20000 bytes before dv: the dense dk (16 KiB) fits, a padded one
     # (row stride 128, 32640 bytes) reaches into dv
@@ -298,3 +298,46 @@ def test_backward_strided_null_and_alias(lib):
     inter[15:18] = [2 * 64 * 128, 64 * 128, 128]
     inter[18:21] = [2 * 64 * 128, 64 * 128, 128]
     assert call_bwd_st(inter, dk=BDQ + 128) == -7
+
+
+# fa_bwd_kv: q-side tensors sized by Sq, k-side by Sk
+GOOD_BWD_KV = dict(GOOD_BWD, Sq=64, Sk=200)
+del GOOD_BWD_KV["S"]
+
+
+def call_bwd_kv(**kw):
+    a = dict(GOOD_BWD_KV)
+    a.update(kw)
+    return fa.fa_bwd_kv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                        a["delta"], a["B"], a["H"], a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"], a["dtype"],
+                        None)
+
+
+# Every case fails validation, so nothing is launched on these fake addresses.
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(k=0), -1), (dict(dk=0), -1), (dict(delta=0), -1), (dict(lse=0), -1),
+    (dict(Sq=-1), -2), (dict(Sk=-1), -2), (dict(causal=2), -2), (dict(d=192), -3), (dict(dtype=5), -4),
+    (dict(scale=-1.0), -5), (dict(dk=BDK + 8), -6), (dict(delta=BDL + 2), -6),
+    # dk spans 2 * 200 * 64 * 2 bytes = 50 KiB: dv 32 KiB after it overlaps
+    (dict(dv=BDK + 32768), -7),
+    # dq spans only 2 * 64 * 64 * 2 = 16 KiB (Sq rows): dk 20 KiB after it is fine, so the
+    # next failure is the alias of dk with dv placed inside it
+    (dict(dk=BDQ + 20480, dv=BDQ + 20480 + 4096), -7),
+    (dict(Sk=1 << 23, d=128, **{n: BASE + (i << 40) for i, n in enumerate(
+        ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta"))}), -8),
+])
+def test_backward_kv_validation_errors(lib, kw, status):
+    assert call_bwd_kv(**kw) == status, fa.fa_status_string(status)
+
+
+def test_backward_kv_empty_sides(lib):
+    # B*H == 0 or Sq = Sk = 0: no-op with every pointer NULL
+    nulls = {n: 0 for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")}
+    assert call_bwd_kv(B=0, **nulls) == 0
+    assert call_bwd_kv(Sq=0, Sk=0, **nulls) == 0
+    # Sq = 0 still writes dk and dv: those (and k, v) must be present
+    assert call_bwd_kv(Sq=0, q=0, o=0, lse=0, dout=0, dq=0, delta=0, dk=0) == -1
+    # Sk = 0 still writes dq and delta: those must be present
+    assert call_bwd_kv(Sk=0, k=0, v=0, dk=0, dv=0, dq=0) == -1
+    # a bad argument is still reported on an empty side
+    assert call_bwd_kv(Sq=0, d=48) == -3
