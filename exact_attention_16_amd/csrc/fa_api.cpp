@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "fa.h"
+#include "fa_bwd_launch.h"
 #include "fa_launch.h"
 
 namespace {

@@ -37,7 +37,7 @@
 #include <stdint.h>
 
 #include "fa_device.h"
-#include "fa_launch.h"
+#include "fa_bwd_launch.h"
 
 namespace fa {
 namespace bwd {
