@@ -123,7 +123,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
                  float scale, int dtype, const long long* strides = nullptr, bool strided = false,
                  bool square = false) {
   if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!forward_head_dim(d)) return FA_ERR_HEAD_DIM;  // the backward takes the same widths
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   if ((long long)B * H == 0 || (square ? Sq == 0 : (Sq == 0 && Sk == 0))) return FA_OK;

@@ -294,6 +294,10 @@ struct DqWave {
         s[sb] = Elem<T>::mma(KT::frag_a(kA, sb, kk, lane), qf[kk], s[sb]);
         dp[sb] = Elem<T>::mma(KT::frag_a(vA, sb, kk, lane), dof[kk], dp[sb]);
       }
+      // wide heads: keep the scheduler from hoisting every k-step's LDS reads
+      // to the top (they would not fit the register file)
+      if constexpr (D > 128)
+        if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
     i16x8 dsf[SB][2];
 #pragma unroll
@@ -313,16 +317,19 @@ struct DqWave {
       pack_c<T>(e, dsf[sb]);
     }
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) dq[db] = Elem<T>::mma(KT::frag_t(kT, db, sb, cc, lane), dsf[sb][cc], dq[db]);
+      if constexpr (D > 128)
+        if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
   }
 };
 
 template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN, bool STRIDED>
-__global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dq_kernel(BwdParams p) {
   using W = DqWave<T, D, CAUSAL, TAIL, NW, BN>;
   using KT = typename W::KT;
   constexpr int BM = NW * 32;
@@ -439,6 +446,7 @@ struct DkvWave {
   template <bool MASKED>
   __device__ __forceinline__ void step(const char* qA, const char* dA, const char* qT, const char* dT,
                                        const float* st, int q0) {
+    if constexpr (D > 128) __builtin_amdgcn_sched_barrier(0);  // no overlap across tiles (registers)
     f32x16 s[QB], dp[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = dp[qb] = f32x16{};
@@ -449,6 +457,8 @@ struct DkvWave {
         s[qb] = Elem<T>::mma(QT::frag_a(qA, qb, kk, lane), kf[kk], s[qb]);
         dp[qb] = Elem<T>::mma(QT::frag_a(dA, qb, kk, lane), vf[kk], dp[qb]);
       }
+      if constexpr (D > 128)  // as in DqWave::step
+        if (kk % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
     i16x8 pf[QB][2], dsf[QB][2];
 #pragma unroll
@@ -476,7 +486,7 @@ struct DkvWave {
       pack_c<T>(de, dsf[qb]);
     }
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -484,6 +494,10 @@ struct DkvWave {
           dv[db] = Elem<T>::mma(QT::frag_t(dT, db, qb, cc, lane), pf[qb][cc], dv[db]);
           dk[db] = Elem<T>::mma(QT::frag_t(qT, db, qb, cc, lane), dsf[qb][cc], dk[db]);
         }
+      if constexpr (D > 128)
+        if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (D > 128) __builtin_amdgcn_sched_barrier(0);
   }
 };
 
@@ -593,7 +607,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
 
 // ------------------------------------------------------------------ launch
 
-constexpr int kDqWaves = 8;
+// Wavefronts per dq_kernel work-group: eight (two per SIMD) up to d = 128;
+// wider heads need a SIMD's whole register file per wavefront.
+template <int D>
+constexpr int dq_waves() { return D > 128 ? 4 : 8; }
 template <int D>
 constexpr int dq_key_tile() { return D == 64 ? 64 : 32; }
 template <int D>
@@ -615,7 +632,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   p.BH = a.B * a.H;
   p.S = a.S;
   p.Sk = a.Sk;
-  p.shift = a.causal ? a.Sk - a.S : 0;
+  // Non-causal: shift = Sk keeps every key (j < Sk <= i + Sk).  The
+  // non-causal instantiations ignore it; wide heads run the causal ones with
+  // it (see launch_bwd_s).
+  p.shift = a.causal ? a.Sk - a.S : a.Sk;
   p.scale = a.scale;
   p.c = a.scale * kLog2e;
   p.H = a.H;
@@ -626,6 +646,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
       p.rs[t] = (uint32_t)(a.strides[3 * t + 2] * 2);
     }
 
+  constexpr int kDqWaves = dq_waves<D>();
   constexpr int BM = kDqWaves * 32;
   constexpr int BN = dq_key_tile<D>();
   // no query rows: no dq_kernel (nothing to write); no key rows: no
@@ -654,7 +675,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
 
 template <typename T, int D, bool STRIDED>
 hipError_t launch_bwd_s(const BwdArgs& a, hipStream_t stream) {
-  return a.causal ? launch_bwd_t<T, D, true, STRIDED>(a, stream) : launch_bwd_t<T, D, false, STRIDED>(a, stream);
+  // Wide heads (d = 192, 256) have only causal instantiations: without a
+  // mask the compiler keeps more fragments in flight than the register file
+  // holds and spills, while the causal code with shift = Sk (every key kept,
+  // so every tile takes the unmasked path) computes the same.
+  if constexpr (D > 128)
+    return launch_bwd_t<T, D, true, STRIDED>(a, stream);
+  else
+    return a.causal ? launch_bwd_t<T, D, true, STRIDED>(a, stream) : launch_bwd_t<T, D, false, STRIDED>(a, stream);
 }
 
 template <typename T, int D>
@@ -664,14 +692,20 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_bwd_dtype(const BwdArgs& a, hipStream_t stream) {
-  return a.d == 64 ? launch_bwd_d<T, 64>(a, stream) : launch_bwd_d<T, 128>(a, stream);
+  switch (a.d) {
+    case 64: return launch_bwd_d<T, 64>(a, stream);
+    case 128: return launch_bwd_d<T, 128>(a, stream);
+    case 192: return launch_bwd_d<T, 192>(a, stream);
+    default: return launch_bwd_d<T, 256>(a, stream);
+  }
 }
 
 }  // namespace bwd
 
 long long bwd_grid_size(const BwdArgs& a) {
   const long long bh = (long long)a.B * a.H;
-  const long long dq = (long long)((a.S + bwd::kDqWaves * 32 - 1) / (bwd::kDqWaves * 32)) * bh;
+  const int bm = (a.d > 128 ? bwd::dq_waves<256>() : bwd::dq_waves<64>()) * 32;
+  const long long dq = (long long)((a.S + bm - 1) / bm) * bh;
   const int bk = (a.d == 64 ? bwd::dkdv_waves<64>() : bwd::dkdv_waves<128>()) * 32;
   const long long dkdv = (long long)((a.Sk + bk - 1) / bk) * bh;
   return dq > dkdv ? dq : dkdv;

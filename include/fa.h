@@ -226,8 +226,8 @@ int fa_fwd_decode_strided(const void* q, const void* k, const void* v, void* o,
  *   delta       [B][H][S] fp32 buffer the call writes D_i into (scratch that
  *               the caller provides, so the library allocates nothing; its
  *               contents on return are D_i).
- *   B, H, S, d, causal, scale, dtype, stream: as for fa_fwd, except that d
- *               must be 64 or 128 (FA_ERR_HEAD_DIM otherwise).
+ *   B, H, S, d, causal, scale, dtype, stream: as for fa_fwd (d = 64, 128,
+ *               192 or 256).
  *
  * Behaviour: as fa_fwd (host validation before any HIP call, asynchronous,
  * no allocation, no state, deterministic: no atomics).  Two kernels are

@@ -103,7 +103,7 @@ def call_bwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), -1), (dict(o=0), -1), (dict(lse=0), -1), (dict(dout=0), -1), (dict(dq=0), -1),
     (dict(dk=0), -1), (dict(dv=0), -1), (dict(delta=0), -1),
-    (dict(B=-1), -2), (dict(causal=3), -2), (dict(d=80), -3), (dict(d=256), -3), (dict(dtype=7), -4),
+    (dict(B=-1), -2), (dict(causal=3), -2), (dict(d=80), -3), (dict(d=320), -3), (dict(dtype=7), -4),
     (dict(scale=float("nan")), -5), (dict(scale=-1.0), -5),
     (dict(dout=BDO + 8), -6), (dict(dq=BDQ + 2), -6), (dict(delta=BDL + 2), -6), (dict(lse=BL_ + 1), -6),
     (dict(dq=BQ_), -7), (dict(dk=BO_ + 64), -7), (dict(dv=BDO + 4096), -7), (dict(delta=BL_), -7),
@@ -316,7 +316,7 @@ def call_bwd_kv(**kw):
 # Every case fails validation, so nothing is launched on these fake addresses.
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), -1), (dict(k=0), -1), (dict(dk=0), -1), (dict(delta=0), -1), (dict(lse=0), -1),
-    (dict(Sq=-1), -2), (dict(Sk=-1), -2), (dict(causal=2), -2), (dict(d=192), -3), (dict(dtype=5), -4),
+    (dict(Sq=-1), -2), (dict(Sk=-1), -2), (dict(causal=2), -2), (dict(d=96), -3), (dict(dtype=5), -4),
     (dict(scale=-1.0), -5), (dict(dk=BDK + 8), -6), (dict(delta=BDL + 2), -6),
     # dk spans 2 * 200 * 64 * 2 bytes = 50 KiB: dv 32 KiB after it overlaps
     (dict(dv=BDK + 32768), -7),

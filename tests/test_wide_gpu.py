@@ -97,3 +97,65 @@ def test_wide_large_sampled(d, causal):
     eo, el = float(np.abs(got_o - so).max()), float(np.abs(got_l - sl).max())
     print(f"wide large d={d}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
     assert eo <= TOL_O and el <= TOL_LSE
+
+
+# ---------------------------------------------------------------- backward
+
+
+def _grads_check(got, ref, label):
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = g.float().cpu().double().numpy()
+        assert np.isfinite(g).all(), f"{label}: {name} not finite"
+        err = float(np.max(np.abs(g - r))) if r.size else 0.0
+        mag = float(np.max(np.abs(r))) if r.size else 0.0
+        print(f"{label} {name}: max|err|={err:.3e} max|ref|={mag:.3e}")
+        assert err <= 2e-2 * mag + 1e-4, f"{label}: {name} max|err| {err} > 2e-2 * {mag} + 1e-4"
+
+
+def _upstream(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed + 777_777)
+    return torch.randn(*shape, generator=g).to(torch.float16 if dtype == "fp16" else torch.bfloat16)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [192, 256])
+@pytest.mark.parametrize("Sq,Sk", [(1, 1), (65, 65), (129, 129), (300, 300), (100, 333), (333, 100)])
+def test_wide_backward_against_oracle(Sq, Sk, d, causal):
+    """Gradients at d = 192 / 256 (fa_bwd / fa_bwd_kv) against the fp64 oracle,
+    every element."""
+    dtype = "fp16" if Sq % 2 else "bf16"
+    label = f"wide bwd Sq={Sq} Sk={Sk} d={d} causal={causal} {dtype}"
+    say(label)
+    q, k, v = make_inputs_kv(2, 2, Sq, Sk, d, dtype, seed=100_000 + Sq + 3 * Sk + d)
+    do = _upstream((2, 2, Sq, d), dtype, Sq + d)
+    scale = default_scale(d)
+    qd, kd, vd, dod = (x.cuda() for x in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    got = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward_kv(to64(q), to64(k), to64(v), to64(do), causal, scale, workers=8)
+    _grads_check(got, ref, label)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_backward_multi_tile_and_strided(causal):
+    """S = 1500 at d = 256 against the oracle; the same gradients through
+    [B, S, H, d] views are bitwise equal."""
+    S, d = 1500, 256
+    say(f"wide bwd S={S} d={d} causal={causal} (+ strided)")
+    q, k, v = make_inputs_kv(1, 2, S, S, d, "bf16", seed=101_000 + causal)
+    do = _upstream((1, 2, S, d), "bf16", 5)
+    scale = default_scale(d)
+    qd, kd, vd, dod = (x.cuda() for x in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    got = fa.backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+
+    def bshd(x):
+        return x.transpose(1, 2).contiguous().transpose(1, 2)
+
+    got_s = fa.backward(bshd(qd), bshd(kd), bshd(vd), bshd(o), lse, bshd(dod), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for g, gs in zip(got, got_s):
+        assert torch.equal(g, gs)
+    ref = oracle.attention_backward(to64(q), to64(k), to64(v), to64(do), causal, scale, workers=8)
+    _grads_check(got, ref, f"wide bwd S={S}")
