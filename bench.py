@@ -327,7 +327,8 @@ def main():
     # more, which the count does not credit.
     backward = []
     if not args.no_backward:
-        for wc in WORKLOADS:
+        # the five workloads, then the wide heads (unless --no-wide)
+        for wc in WORKLOADS + (() if args.no_wide else WIDE):
             steps = max(5, min(args.steps, int(2e9 / max(1.0, 2.5 * flops(wc) / 1e3))))
             rb = time_backward(wc, steps, args.warmup)
             msb = rb["total_ms"] / steps
