@@ -51,17 +51,24 @@ def _run(cmd: list[str], verbose: bool) -> None:
         print(msgs)
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source for gfx950 and link libfa.so in-tree."""
+def build(verbose: bool = False, extra: list[str] | None = None, jobs: int | None = None) -> str:
+    """Compile every source for gfx950 (in parallel, one hipcc per source) and
+    link libfa.so in-tree."""
+    from concurrent.futures import ThreadPoolExecutor
+
     cc = hipcc()
-    objs = []
     obj_dir = os.path.join(PKG, "_obj")
     os.makedirs(obj_dir, exist_ok=True)
+    cmds, objs = [], []
     for src, flags in SOURCES:
         obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-        _run([cc, f"--offload-arch={ARCH}", *COMMON, *flags, "-I", INCLUDE, "-I", CSRC,
-              "-c", os.path.join(CSRC, src), "-o", obj] + list(extra or []), verbose)
+        cmds.append([cc, f"--offload-arch={ARCH}", *COMMON, *flags, "-I", INCLUDE, "-I", CSRC,
+                     "-c", os.path.join(CSRC, src), "-o", obj] + list(extra or []))
         objs.append(obj)
+    jobs = jobs or max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()  # re-raises the first failure
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
