@@ -16,7 +16,7 @@ namespace {
 thread_local char g_last_hip_error[256] = "";
 
 // Head dimensions of the forward and decoding kernels (the backward: 64, 128).
-bool forward_head_dim(int d) { return d == 64 || d == 128 || d == 192 || d == 256; }
+bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 192 || d == 256; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (na == 0 || nb == 0) return false;  // an empty range overlaps nothing
@@ -79,7 +79,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
              int S, int Sk, int d, int causal, float scale, int dtype, const long long* strides = nullptr,
              bool strided = false, Extents* ext = nullptr) {
   if (B < 0 || H < 0 || S < 0 || Sk < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
-  if (!forward_head_dim(d)) return FA_ERR_HEAD_DIM;
+  if (!supported_head_dim(d)) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   if ((long long)B * H * S == 0) return FA_OK;  // empty problem: nothing to touch
@@ -123,7 +123,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
                  float scale, int dtype, const long long* strides = nullptr, bool strided = false,
                  bool square = false) {
   if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || (causal != 0 && causal != 1)) return FA_ERR_SHAPE;
-  if (!forward_head_dim(d)) return FA_ERR_HEAD_DIM;  // the backward takes the same widths
+  if (!supported_head_dim(d)) return FA_ERR_HEAD_DIM;  // the backward takes the same widths
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
   if ((long long)B * H == 0 || (square ? Sq == 0 : (Sq == 0 && Sk == 0))) return FA_OK;
@@ -269,7 +269,7 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* 
 }
 
 size_t fa_fwd_decode_workspace_size(int B, int H, int Sq, int Sk, int d) {
-  if (B <= 0 || H <= 0 || Sq <= 0 || Sk < 0 || !forward_head_dim(d)) return 0;
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk < 0 || !supported_head_dim(d)) return 0;
   fa::DecodeArgs a{};
   a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
   return fa::decode_plan(a).workspace_bytes;

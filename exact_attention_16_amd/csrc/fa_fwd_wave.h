@@ -265,12 +265,7 @@ struct FwdWave {
   }
 
   template <bool MASKED>
-  __device__ __forceinline__ void softmax_impl(int k0) { softmax_on<MASKED>(k0, sacc); }
-
-  // The update on scores held in `sacc` (this wavefront's own, or a second
-  // score buffer of a pipelined schedule).
-  template <bool MASKED>
-  __device__ __forceinline__ void softmax_on(int k0, f32x16 (&sacc)[SB]) {
+  __device__ __forceinline__ void softmax_impl(int k0) {
     if (MASKED) {
       // key k0 + t + 4h (t below) is kept iff t < Sk - k0 - 4h and, when
       // causal, t <= myq + shift - k0 - 4h
