@@ -89,6 +89,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   if ((long long)S * d >= (1LL << 30) || (long long)Sk * d >= (1LL << 30)) return FA_ERR_TOO_LARGE;  // 32-bit buffer offsets
   fa::FwdArgs a{};
   a.B = B; a.H = H; a.S = S; a.Sk = Sk; a.d = d;
+  a.causal = causal != 0;  // the kernel (and so the grid) depends on it
   if (fa::fwd_grid_size(a) > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
   Layout lq = dense_layout(H, S, d), lk = dense_layout(H, Sk, d), lv = lk, lo = lq;
   if (strided) {

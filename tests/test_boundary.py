@@ -341,3 +341,13 @@ def test_backward_kv_empty_sides(lib):
     assert call_bwd_kv(Sk=0, k=0, v=0, dk=0, dv=0, dq=0) == -1
     # a bad argument is still reported on an empty side
     assert call_bwd_kv(Sq=0, d=48) == -3
+
+
+def test_grid_check_follows_the_kernel_choice(lib):
+    # causal S = 129 at d = 64 runs the in-order kernel (128-row blocks: 2 per
+    # head); 2^30 heads then need 2^31 work-groups, one more than a launch can
+    # take.  Non-causal runs 256-row blocks (1 per head) and passes the grid
+    # check, failing later on the (fake) pointers' overlap instead.
+    big = dict(B=1 << 15, H=1 << 15, S=129, d=64)
+    assert call(causal=1, **big) == -8
+    assert call(causal=0, **big) == -7
