@@ -653,10 +653,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   // dkdv_kernel (the dq_kernel then writes dq = 0 and delta)
   p.nblk = (a.S + BM - 1) / BM;
   const bool tail = a.Sk % BN != 0;
+  // A ragged non-causal d = 128 problem runs the causal tail variant (shift
+  // = Sk keeps every key): the non-causal one spills.
+  constexpr bool kTailCausal = CAUSAL || D == 128;
   if (p.nblk > 0) {
     if (tail)
-      hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, true, kDqWaves, BN, STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
-                         dim3(kDqWaves * 64), 0, stream, p);
+      hipLaunchKernelGGL((dq_kernel<T, D, kTailCausal, true, kDqWaves, BN, STRIDED>),
+                         dim3((unsigned)(p.nblk * p.BH)), dim3(kDqWaves * 64), 0, stream, p);
     else
       hipLaunchKernelGGL((dq_kernel<T, D, CAUSAL, false, kDqWaves, BN, STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
                          dim3(kDqWaves * 64), 0, stream, p);
