@@ -1,15 +1,18 @@
 """Attention-forward benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--no-per-config] [--no-sweep]
-                    [--no-backward] [--no-decode] [--no-wide] [--decode NAMES]
-                    [--copy-calibration]
+                    [--no-cpu-baseline] [--no-per-config] [--no-parity]
+                    [--no-sweep] [--no-backward] [--no-decode] [--no-wide]
+                    [--decode NAMES] [--copy-calibration]
 
 One step is one exact-attention forward pass (every step of the method, one
 kernel launch) over one batch of the workload's synthetic inputs, already
 resident in device memory.  The default workload is the short-sequence batch
-(B=32, H=32, S=512, d=64, bf16, no mask: 16k tokens); all five workloads are
-also timed and reported under "per_config", the pages' benchmark grid
+(B=32, H=32, S=512, d=64, bf16, no mask: 16k tokens).  All five workloads are
+also timed (at least 20 launches each) and reported under "per_config", the
+last key of the line: each with min / median / p90 launch times, its
+roofline, and the max-abs errors of its outputs against the whole fp64 oracle,
+which is timed on the host cores beside it.  The pages' benchmark grid
 (S 512..16k x d 64/128 x causal, 16k tokens, bf16) under "sweep", and the
 gradients (fa_bwd) of the five workloads under "backward", and the split-key
 decoding pass (fa_fwd_decode) over three 1 GiB K/V caches under "decode", and
@@ -38,7 +41,7 @@ PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 40
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")]
+                  for f in ("fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")]
 DECODE_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
                   for f in ("fa_decode.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_fa_fwd.md")
@@ -80,7 +83,22 @@ def recorded_traffic(workload: str, record: str = TRAFFIC_RECORD, sources=None):
     return None
 
 
-def time_workload(w, steps: int, warmup: int, per_launch: bool = False):
+def progress(msg: str) -> None:
+    """One line per finished piece of work, on stderr (stdout holds only the
+    JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_workload(w, steps: int, warmup: int, per_launch: bool = False, keep_outputs: bool = False):
+    """Time `steps` forward launches of workload `w` (inputs and outputs
+    resident in device memory).
+
+    total_ms: K back-to-back launches between two events on the launch stream
+    (the step time; no marker between launches).  With per_launch, a second
+    sequence of K launches has an event before and after each launch
+    (K + 1 events, still back to back apart from the markers): min / median /
+    p90 / mean of those per-launch durations.  keep_outputs returns O (fp32)
+    and LSE of the last launch as host arrays, for the parity check."""
     import torch
 
     import exact_attention_16_amd as fa
@@ -91,11 +109,10 @@ def time_workload(w, steps: int, warmup: int, per_launch: bool = False):
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=q.device)
     scale = default_scale(w.d)
     stream = torch.cuda.current_stream()
+    torch.cuda.reset_peak_memory_stats()
     for _ in range(warmup):
         fa.forward(q, k, v, causal=w.causal, scale=scale, out=out, lse=lse, stream=stream)
     torch.cuda.synchronize()
-    # Two events bracket the K back-to-back launches on the launch stream (a
-    # marker between launches would add its own gap to every step).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
@@ -105,25 +122,26 @@ def time_workload(w, steps: int, warmup: int, per_launch: bool = False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    launch_ms = None
     launch_stats = None
     if per_launch:
-        # For reference only: a second pass of K launches, each between its
-        # own pair of events on the launch stream (launches that do not run
-        # back to back; on the MI355X they run shorter than back-to-back ones).
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for a, b in evs:
-            a.record(stream)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(stream)
+        for i in range(steps):
             fa.forward(q, k, v, causal=w.causal, scale=scale, out=out, lse=lse, stream=stream)
-            b.record(stream)
+            evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        per = sorted(a.elapsed_time(b) for a, b in evs)
-        launch_ms = sum(per) / steps
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
         launch_stats = {"min_ms": per[0], "median_ms": per[len(per) // 2],
-                        "p90_ms": per[min(len(per) - 1, int(0.9 * len(per)))]}
+                        "p90_ms": per[min(len(per) - 1, int(0.9 * len(per)))], "mean_ms": sum(per) / steps}
     ok = bool(torch.isfinite(lse).all().item())
+    res = dict(total_ms=total_ms, wall_s=wall, finite=ok, launch_stats=launch_stats,
+               peak_mem_mib=torch.cuda.max_memory_allocated() / 2**20)
+    if keep_outputs:
+        res["o"] = out.float().cpu().numpy()
+        res["lse"] = lse.cpu().numpy()
     del q, k, v, out, lse
-    return dict(total_ms=total_ms, wall_s=wall, finite=ok, launch_ms=launch_ms, launch_stats=launch_stats)
+    progress(f"forward {w.name}: {total_ms / steps:.4f} ms per launch over {steps}")
+    return res
 
 
 def time_backward(w, steps: int, warmup: int):
@@ -154,6 +172,7 @@ def time_backward(w, steps: int, warmup: int):
     end.record(stream)
     torch.cuda.synchronize()
     ok = all(bool(torch.isfinite(t.float()).all().item()) for t in (dq, dk, dv))
+    progress(f"backward {w.name}: {start.elapsed_time(end) / steps:.4f} ms per step")
     return dict(total_ms=start.elapsed_time(end), finite=ok)
 
 
@@ -189,6 +208,7 @@ def time_decode(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     ok = bool(torch.isfinite(lse).all().item()) and bool(torch.isfinite(out.float()).all().item())
     del q, k, v
+    progress(f"decode {w.name}: {start.elapsed_time(end) / steps:.4f} ms per call")
     return dict(total_ms=start.elapsed_time(end), finite=ok, workspace_bytes=ws.numel())
 
 
@@ -217,6 +237,7 @@ def cpu_baseline(w, budget_heads: int, min_seconds: float = 10.0):
         if dt >= min_seconds:
             break
     assert np.isfinite(o).all() and np.isfinite(l).all()
+    progress(f"cpu baseline: {runs} oracle run(s) in {dt:.1f} s")
     sample = w.scaled(B=b_n, H=h_n)
     return {
         "value": runs * flops(sample) / dt / 1e12,
@@ -243,6 +264,60 @@ def copy_calibration(steps: int):
     return {"copy_bytes": n, "copies": steps}
 
 
+def _r(x, nd=4):
+    """A float rounded to `nd` significant digits (keeps the JSON line short)."""
+    if x is None:
+        return None
+    return float(f"{x:.{nd}g}")
+
+
+def roofline(w, launch_ms: float) -> dict:
+    """The roofline object of one forward workload: its bound by arithmetic
+    intensity against the ridge point, the achieved rate on the algorithmic
+    work per launch, and the recorded HBM traffic (null once the kernel
+    source changed since the counters were taken)."""
+    f, nbytes = flops(w), algorithmic_bytes(w)
+    t = launch_ms * 1e-3
+    if f / nbytes < RIDGE:
+        achieved = nbytes / t / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = f / t / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_TFLOPS}
+    roof["traffic"] = recorded_traffic(w.name)
+    return roof
+
+
+def oracle_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def oracle_parity(w, o_gpu, lse_gpu) -> dict:
+    """The whole fp64 oracle on the workload's inputs (timed on the host
+    cores), and the max-abs errors of the GPU's O and LSE against it:
+    err_o, err_lse, ok (both within 2e-2 / 1e-3), oracle_s, cores."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_16_amd.inputs import default_scale, make_inputs
+
+    q, k, v = (x.double().numpy() for x in make_inputs(w))
+    workers = oracle_workers()
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.attention(q, k, v, w.causal, default_scale(w.d), workers=workers)
+    dt = time.perf_counter() - t0
+    eo = float(np.abs(o_gpu.astype(np.float64) - o_ref).max())
+    el = float(np.abs(lse_gpu.astype(np.float64) - lse_ref).max())
+    progress(f"oracle {w.name}: {dt:.1f} s on {workers} threads, max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    return {"err_o": eo, "err_lse": el, "ok": bool(eo <= 2e-2 and el <= 1e-3), "oracle_s": dt, "cores": workers}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +326,7 @@ def main():
     ap.add_argument("--workload", default="short_seq_batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--no-parity", action="store_true", help="skip the per-config oracle runs")
     ap.add_argument("--no-sweep", action="store_true", help="skip the S x d x causal grid")
     ap.add_argument("--no-backward", action="store_true", help="skip the gradient timings")
     ap.add_argument("--no-decode", action="store_true", help="skip the split-key decoding timings")
@@ -287,62 +363,48 @@ def main():
     ms = r["total_ms"] / args.steps
     f = flops(w)
     value = f / (ms * 1e-3) / 1e12
-    avg_launch_s = ms * 1e-3  # back-to-back launches run contiguously: step time = launch duration
-    ai = f / algorithmic_bytes(w)
-    bytes_pl = algorithmic_bytes(w)
-    if ai < RIDGE:
-        achieved = bytes_pl / avg_launch_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS}
-    else:
-        achieved = f / avg_launch_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_MFMA_TFLOPS}
-    roof["traffic"] = recorded_traffic(w.name)
-    roof["algorithmic_bytes"] = bytes_pl
+    # back-to-back launches run contiguously (rocprofv3 trace), so the step
+    # time is the kernel's average launch duration
+    roof = roofline(w, ms)
+    roof["algorithmic_bytes"] = algorithmic_bytes(w)
     roof["flops"] = f
     roof["mfma_frac"] = value / PEAK_MFMA_TFLOPS
     roof["kernel"] = "fa::detail::fwd_kernel"
-    roof["launch_ms"] = ms                          # the timed back-to-back launches
-    roof["isolated_launch_ms"] = r["launch_ms"]     # the same kernel between per-launch event pairs
-    roof["isolated_launch_stats"] = r["launch_stats"]
+    roof["launch_ms"] = ms
+    roof["launch_stats"] = r["launch_stats"]
 
     def time_list(workloads):
-        out = []
+        out = {}
         for wc in workloads:
             steps = max(5, min(args.steps, int(2e9 / max(1.0, flops(wc) / 1e3))))
             rc = time_workload(wc, steps, args.warmup)
             msc = rc["total_ms"] / steps
             tf = flops(wc) / (msc * 1e-3) / 1e12
-            out.append({"workload": wc.name, "B": wc.B, "H": wc.H, "S": wc.S, "d": wc.d,
-                        "dtype": wc.dtype, "causal": wc.causal, "ms": msc,
-                        "tflops": tf, "pct_peak": 100.0 * tf / PEAK_MFMA_TFLOPS,
-                        "steps": steps, "finite": rc["finite"]})
+            out[wc.name] = {"ms": _r(msc), "tflops": _r(tf), "pct": _r(100.0 * tf / PEAK_MFMA_TFLOPS),
+                            "steps": steps, "finite": rc["finite"]}
         return out
 
-    per_config = [] if args.no_per_config else time_list(WORKLOADS)
     # Gradients of every workload (fa_bwd, two kernels per step).  FLOPs by
     # the usual count for the attention backward: 2.5x the forward (five
     # S x S x d products instead of two); the kernels recompute S and dP once
     # more, which the count does not credit.
-    backward = []
+    backward = {}
     if not args.no_backward:
-        # the five workloads, then the wide heads (unless --no-wide)
         for wc in WORKLOADS + (() if args.no_wide else WIDE):
             steps = max(5, min(args.steps, int(2e9 / max(1.0, 2.5 * flops(wc) / 1e3))))
             rb = time_backward(wc, steps, args.warmup)
             msb = rb["total_ms"] / steps
             tf = 2.5 * flops(wc) / (msb * 1e-3) / 1e12
-            backward.append({"workload": wc.name, "ms": msb, "tflops": tf,
-                             "pct_peak": 100.0 * tf / PEAK_MFMA_TFLOPS, "steps": steps, "finite": rb["finite"]})
+            backward[wc.name] = {"ms": _r(msb), "tflops": _r(tf), "pct": _r(100.0 * tf / PEAK_MFMA_TFLOPS),
+                                 "steps": steps, "finite": rb["finite"]}
     # The pages' kernel-benchmark grid (S 512..16k x d 64/128 x causal, 16k
     # tokens per batch), bf16.
-    sweep = [] if args.no_sweep else time_list(SWEEP)
+    sweep = {} if args.no_sweep else time_list(SWEEP)
     # Wide heads (d = 192, 256: four-wavefront work-groups), beyond the grid.
-    wide = [] if args.no_wide else time_list(WIDE)
+    wide = {} if args.no_wide else time_list(WIDE)
     # Token-by-token decoding (fa_fwd_decode: split pass + merge per step),
     # bound by HBM: reported against the 8 TB/s peak.
-    decode = []
+    decode = {}
     if not args.no_decode:
         names = [n for n in args.decode.split(",") if n]
         for wd in DECODE:
@@ -352,11 +414,43 @@ def main():
             rd = time_decode(wd, steps, args.warmup)
             msd = rd["total_ms"] / steps
             gbs = decode_bytes(wd) / (msd * 1e-3) / 1e9
-            decode.append({"workload": wd.name, "B": wd.B, "H": wd.H, "Sq": wd.Sq, "Sk": wd.Sk, "d": wd.d,
-                           "causal": wd.causal, "ms": msd, "algorithmic_bytes": decode_bytes(wd),
-                           "gbs": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "steps": steps,
-                           "workspace_bytes": rd["workspace_bytes"], "finite": rd["finite"],
-                           "traffic": recorded_traffic(wd.name, DECODE_TRAFFIC_RECORD, DECODE_SOURCES)})
+            tr = recorded_traffic(wd.name, DECODE_TRAFFIC_RECORD, DECODE_SOURCES)
+            decode[wd.name] = {"ms": _r(msd), "gbs": _r(gbs), "frac_hbm": _r(gbs / PEAK_HBM_GBS),
+                               "algorithmic_bytes": decode_bytes(wd), "traffic": _r(tr), "steps": steps,
+                               "finite": rd["finite"]}
+
+    # The five workloads, each: >= 20 timed back-to-back launches (their mean
+    # is the step time "ms") and a second marked sequence for min / median /
+    # p90; its roofline (achieved in the bound's unit: GB/s for "hbm",
+    # TFLOP/s for "mfma"; traffic = recorded HBM bytes per launch); peak
+    # device memory; the outputs of the timed launches against the whole
+    # fp64 oracle, which is timed on the host cores (oracle_s on `cores`
+    # threads; it computes every score, causal or not).  GPU timings come
+    # first, the oracle runs after all of them.
+    per_config = []
+    if not args.no_per_config:
+        outs = []
+        for wc in WORKLOADS:
+            steps = max(20, args.steps)
+            rc = time_workload(wc, steps, args.warmup, per_launch=True, keep_outputs=not args.no_parity)
+            msc = rc["total_ms"] / steps
+            tf = flops(wc) / (msc * 1e-3) / 1e12
+            roof_c = roofline(wc, msc)
+            st = rc["launch_stats"]
+            per_config.append({
+                "workload": wc.name, "shape": f"B{wc.B} H{wc.H} S{wc.S} d{wc.d}", "dtype": wc.dtype,
+                "causal": wc.causal, "steps": steps, "ms": _r(msc), "ms_min": _r(st["min_ms"]),
+                "ms_median": _r(st["median_ms"]), "ms_p90": _r(st["p90_ms"]), "tflops": _r(tf),
+                "pct_peak": _r(100.0 * tf / PEAK_MFMA_TFLOPS),
+                "roofline": {"bound": roof_c["bound"], "achieved": _r(roof_c["achieved"]),
+                             "frac": _r(roof_c["frac"]), "traffic": _r(roof_c["traffic"])},
+                "mem_mib": _r(rc["peak_mem_mib"])})
+            outs.append((rc.get("o"), rc.get("lse")))
+        if not args.no_parity:
+            for entry, wc, (o_gpu, lse_gpu) in zip(per_config, WORKLOADS, outs):
+                par = oracle_parity(wc, o_gpu, lse_gpu)
+                entry.update({k: (_r(v, 3) if isinstance(v, float) else v) for k, v in par.items()})
+            del outs
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -381,15 +475,16 @@ def main():
                    "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_TFLOPS},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "per_config": per_config,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", ""), "rocm": torch.version.hip},
+        "wall_s_timed_region": r["wall_s"],
+        "outputs_finite": r["finite"],
         "sweep": sweep,
         "backward": backward,
         "decode": decode,
         "wide": wide,
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "gcn_arch": getattr(props, "gcnArchName", "")},
-        "wall_s_timed_region": r["wall_s"],
-        "outputs_finite": r["finite"],
+        # last, so that a reader of the line's tail sees the five workloads
+        "per_config": per_config,
     }
     print(json.dumps(line), flush=True)
 

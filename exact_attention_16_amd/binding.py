@@ -181,6 +181,14 @@ def _layout(*ts):
     return out
 
 
+def _on_device(device, **named):
+    """Every named tensor must live in device memory on ``device`` (the
+    kernels read and write them there; a host pointer would fault)."""
+    for name, t in named.items():
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be a device tensor on {device}, got {t.device}")
+
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
             scale: float | None = None, out: torch.Tensor | None = None,
             lse: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None):
@@ -200,7 +208,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
                          f"{tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
         raise TypeError("q, k, v must all be float16 or all bfloat16")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not q.is_cuda:
         raise ValueError("q, k, v must be device tensors")
     B, H, S, d = q.shape
     Sk = k.shape[2]
@@ -210,6 +218,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _on_device(q.device, k=k, v=v, out=out, lse=lse)
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must be a tensor like q")
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -250,7 +259,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
                          f"{tuple(k.shape)}, {tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
         raise TypeError("q, k, v must all be float16 or all bfloat16")
-    if not all(t.is_cuda for t in (q, k, v)):
+    if not q.is_cuda:
         raise ValueError("q, k, v must be device tensors")
     B, H, Sq, d = q.shape
     Sk = k.shape[2]
@@ -258,6 +267,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
         scale = float(torch.tensor(d, dtype=torch.float32).rsqrt())
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _on_device(q.device, k=k, v=v, out=out, lse=lse)
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must be a tensor like q")
     if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -265,7 +275,8 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
     need = fa_fwd_decode_workspace_size(B, H, Sq, Sk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not (workspace.is_cuda and workspace.is_contiguous()):
+    _on_device(q.device, workspace=workspace)
+    if not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
@@ -311,8 +322,9 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         raise ValueError("q, o, dout must be [B, H, Sq, d] and k, v [B, H, Sk, d]")
     if any(t.dtype != q.dtype for t in ts) or q.dtype not in _DTYPES:
         raise TypeError("q, k, v, o, dout must all be float16 or all bfloat16")
-    if not all(t.is_cuda for t in ts):
+    if not q.is_cuda:
         raise ValueError("q, k, v, o, dout must be device tensors")
+    _on_device(q.device, k=k, v=v, o=o, dout=dout, lse=lse)
     if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
     if scale is None:
@@ -323,8 +335,9 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dv = torch.empty_like(k) if dv is None else dv
     if delta is None:
         delta = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _on_device(q.device, dq=dq, dk=dk, dv=dv, delta=delta)
     for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
-        if t.shape != like.shape or t.dtype != q.dtype or not t.is_cuda:
+        if t.shape != like.shape or t.dtype != q.dtype:
             raise ValueError(f"{name} must be a device tensor shaped like {'q' if like is q else 'k'}")
     if delta.shape != (B, H, Sq) or delta.dtype != torch.float32 or not delta.is_contiguous():
         raise ValueError("delta must be a contiguous float32 [B, H, Sq] tensor")

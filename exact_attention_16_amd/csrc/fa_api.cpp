@@ -15,7 +15,7 @@ namespace {
 
 thread_local char g_last_hip_error[256] = "";
 
-// Head dimensions of the forward and decoding kernels (the backward: 64, 128).
+// Head dimensions of every entry point (forward, decoding and backward kernels).
 bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 192 || d == 256; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -314,7 +314,7 @@ const char* fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a pointer argument is NULL";
     case FA_ERR_SHAPE: return "B, H, S or Sk is negative, or causal is not 0 or 1";
-    case FA_ERR_HEAD_DIM: return "head dimension d must be 64, 128, 192 or 256 (fa_bwd: 64 or 128)";
+    case FA_ERR_HEAD_DIM: return "head dimension d must be 64, 128, 192 or 256";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
     case FA_ERR_ALIGN:

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(NW * 64, (decode_waves_per_simd<D, NW, BPW, CAUSAL 
   {
     const float ltot = sum_with_partner(w.lsum);
     const bool none = !(ltot > 0.f);
-    const float inv = none ? 0.f : 1.0f / ltot;
+    const float inv = none ? 0.f : 1.0f / w.out_divisor();
 #pragma unroll
     for (int db = 0; db < DB; ++db) w.oacc[db] *= inv;
     lse_w = none ? -__builtin_inff() : (w.mc + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f;

@@ -43,6 +43,15 @@ struct Elem<__bf16> {
     bf16x2 r = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(unsigned, r);
   }
+  // The weights rounded to bf16 keep 8 significant bits, so the output is
+  // normalised by the sum of the ROUNDED weights (acc + both halves of a
+  // packed pair, one v_dot2): a weight's rounding error then cancels between
+  // numerator and denominator instead of scaling the whole output row.
+  static constexpr bool kRoundedSum = true;
+  static __device__ __forceinline__ float add_packed(unsigned w, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+  }
 };
 
 template <>
@@ -55,6 +64,10 @@ struct Elem<_Float16> {
     f16x2 r = {(_Float16)x, (_Float16)y};
     return __builtin_bit_cast(unsigned, r);
   }
+  // fp16 weights keep 11 significant bits: the exact fp32 row sum serves both
+  // the output and the logsumexp.
+  static constexpr bool kRoundedSum = false;
+  static __device__ __forceinline__ float add_packed(unsigned, float acc) { return acc; }
 };
 
 struct Params {
@@ -99,10 +112,13 @@ __device__ __forceinline__ float max_with_partner(float x) { return fmaxf(x, par
 
 __device__ __forceinline__ float sum_with_partner(float x) { return x + partner_value(x); }
 
-// Work-group barrier without a memory fence: the waits each step needs are
-// explicit (s_waitcnt), and the "memory" clobber keeps the compiler from
-// moving LDS accesses across it.
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Work-group barrier.  It first waits for this wavefront's own LDS accesses
+// (lgkmcnt(0)): an LDS read still in flight could otherwise see a buffer that
+// another wavefront refills after the barrier, and an LDS write might not yet
+// be visible to the wavefronts that read it after the barrier.  Waits for
+// vector memory (vmcnt) are explicit at each call site, and the "memory"
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 }  // namespace detail
 }  // namespace fa

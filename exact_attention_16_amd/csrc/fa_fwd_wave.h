@@ -89,7 +89,8 @@ struct FwdWave {
   i16x8 pf[SB][2];   // its weights between the softmax and the P V MFMAs
   float m_used;      // reference max (raw score units) the weights are taken against
   float mc;          // c * m_used
-  float lsum;        // this lane's share of the row sum
+  float lsum;        // this lane's share of the row sum (fp32 weights: the logsumexp)
+  float lsum_o;      // bf16: its share of the sum of the rounded weights (the output's divisor)
 
   // Lengths, scale, the head's Q/K/V/O bases and ranges from the launch
   // parameters, then this lane's Q row (qw, myq and the lane fields must be
@@ -143,6 +144,7 @@ struct FwdWave {
     m_used = -__builtin_inff();
     mc = 0.f;
     lsum = 0.f;
+    lsum_o = 0.f;
   }
 
   // HBM -> LDS copies of one key tile (BN rows of K, or of V), issued
@@ -303,12 +305,15 @@ struct FwdWave {
       m_used = m_new;
       mc = c * m_new;
       lsum *= alpha;
+      if constexpr (Elem<T>::kRoundedSum) lsum_o *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
 
-    // weights; the row sum is kept in four partial sums (independent chains)
+    // weights; the row sum is kept in four partial sums (independent chains),
+    // the bf16 sum of the rounded weights in two
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    float lo[2] = {0.f, 0.f};
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) {
       float e[16];
@@ -322,11 +327,16 @@ struct FwdWave {
       for (int cc = 0; cc < 2; ++cc) {
         u32x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = Elem<T>::pack(e[8 * cc + 2 * i], e[8 * cc + 2 * i + 1]);
+        for (int i = 0; i < 4; ++i) {
+          const unsigned x = Elem<T>::pack(e[8 * cc + 2 * i], e[8 * cc + 2 * i + 1]);
+          w[i] = x;
+          if constexpr (Elem<T>::kRoundedSum) lo[i & 1] = Elem<T>::add_packed(x, lo[i & 1]);
+        }
         pf[sb][cc] = __builtin_bit_cast(i16x8, w);
       }
     }
     lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    if constexpr (Elem<T>::kRoundedSum) lsum_o += lo[0] + lo[1];
   }
 
   // Phase MFMA(k): P_{k-1} V_{k-1} (V from vp) and K_k Q^T (K from kc).
@@ -342,13 +352,19 @@ struct FwdWave {
     if (k >= 0 && k < n && active(k * BN)) softmax(k * BN);
   }
 
-  // O = O_acc / l and LSE = (c m + log2 l) ln 2; rows >= S are dropped by the
-  // descriptors' range checks.  A row that saw no key (causal, more query
-  // rows than keys) has l = 0: it stores O = 0 and LSE = -inf.
+  // The sum the output is divided by (the rounded weights' for bf16).
+  __device__ __forceinline__ float out_divisor() const {
+    return sum_with_partner(Elem<T>::kRoundedSum ? lsum_o : lsum);
+  }
+
+  // O = O_acc / out_divisor() and LSE = (c m + log2 l) ln 2 with the fp32 row
+  // sum l; rows >= S are dropped by the descriptors' range checks.  A row
+  // that saw no key (causal, more query rows than keys) has l = 0: it stores
+  // O = 0 and LSE = -inf.
   __device__ __forceinline__ void store(void* o, float* lse, size_t head_elems, int bh) const {
     const float ltot = sum_with_partner(lsum);
     const bool none = !(ltot > 0.f);
-    const float inv = none ? 0.f : 1.0f / ltot;
+    const float inv = none ? 0.f : 1.0f / out_divisor();
     const __amdgpu_buffer_rsrc_t ro =
         STRIDED ? rsrc(oh, o_bytes) : rsrc((const char*)o + head_elems * 2, head_bytes);
 #pragma unroll

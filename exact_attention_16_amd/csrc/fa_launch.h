@@ -71,7 +71,7 @@ struct DecodeArgs {
 // d = 64 and 64 keys at d = 128 (32 KiB of K and V per work-group), and about
 // two work-groups per compute unit, read the caches fastest; more resident
 // work-groups (more concurrent streams) read them more slowly.
-constexpr int decode_waves(int d) { return d == 64 ? 2 : 2; }
+constexpr int decode_waves(int) { return 2; }
 constexpr int decode_blocks_per_wave(int d) { return d == 64 ? 2 : 1; }
 constexpr int decode_tile_keys(int d) { return 32 * decode_waves(d) * decode_blocks_per_wave(d); }
 constexpr long long kDecodeTargetGroups = 512;

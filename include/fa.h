@@ -39,7 +39,7 @@ enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a pointer argument is NULL (non-empty problem)       */
   FA_ERR_SHAPE = -2,     /* B, H, S or Sk negative, or causal not 0/1            */
-  FA_ERR_HEAD_DIM = -3,  /* d not 64/128/192/256 (fa_bwd: not 64/128)          */
+  FA_ERR_HEAD_DIM = -3,  /* d not 64, 128, 192 or 256 (every entry point)       */
   FA_ERR_DTYPE = -4,     /* dtype is not an fa_dtype value                       */
   FA_ERR_SCALE = -5,     /* scale is NaN, infinite or negative                   */
   FA_ERR_ALIGN = -6,     /* a tensor (or a stride) not 16-byte aligned, or lse/delta not 4-byte */
@@ -180,8 +180,8 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o,
 /*
  * Workspace bytes fa_fwd_decode needs for these shapes (a pure function of
  * its arguments: the key split is chosen from the shapes alone).  Returns 0
- * when B*H*Sq == 0 or the arguments are invalid (d not 64/128, a negative
- * size); then fa_fwd_decode needs no workspace or fails validation.
+ * when B*H*Sq == 0 or the arguments are invalid (d not 64, 128, 192 or 256,
+ * a negative size); then fa_fwd_decode needs no workspace or fails validation.
  */
 size_t fa_fwd_decode_workspace_size(int B, int H, int Sq, int Sk, int d);
 

@@ -4,6 +4,7 @@ The HIP path is always reached through the C ABI (``exact_attention_16_amd``'s
 ctypes binding); the expected values always come from the CPU oracle.
 """
 
+import os
 import sys
 
 import numpy as np
@@ -16,6 +17,16 @@ import oracle
 # against the fp64 oracle, for fp16/bf16 inputs with fp32 accumulation.
 TOL_O = 2e-2
 TOL_LSE = 1e-3
+
+
+def oracle_workers() -> int:
+    """Threads for the oracle: the host cores this process may use, at most
+    16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def say(msg):
@@ -45,7 +56,7 @@ def check_full(q, k, v, causal, scale, label=""):
     """Whole-tensor parity: every element of O and LSE against the oracle."""
     say(f"full {label} shape={tuple(q.shape)} dtype={q.dtype} causal={causal}")
     o, lse = gpu_forward(q, k, v, causal, scale)
-    o_ref, lse_ref = oracle.attention(to64(q), to64(k), to64(v), causal, scale, workers=8)
+    o_ref, lse_ref = oracle.attention(to64(q), to64(k), to64(v), causal, scale, workers=oracle_workers())
     eo, el = errors(o.float().cpu().double().numpy(), lse.cpu().double().numpy(), o_ref, lse_ref)
     assert np.isfinite(eo) and np.isfinite(el), (eo, el)
     assert eo <= TOL_O, f"{label}: max |O - O_ref| = {eo}"

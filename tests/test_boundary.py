@@ -351,3 +351,37 @@ def test_grid_check_follows_the_kernel_choice(lib):
     big = dict(B=1 << 15, H=1 << 15, S=129, d=64)
     assert call(causal=1, **big) == -8
     assert call(causal=0, **big) == -7
+
+
+def test_binding_rejects_host_tensors_before_any_call(monkeypatch):
+    """Every tensor the kernels touch must be device memory on q's device:
+    the binding raises ValueError before reaching any C entry point (a host
+    pointer passed through would fault the GPU)."""
+    import types
+
+    import torch
+
+    def no_call(*a, **k):
+        raise AssertionError("the C entry point must not be reached")
+
+    for name in ("fa_fwd", "fa_fwd_kv", "fa_fwd_strided", "fa_fwd_decode", "fa_fwd_decode_strided", "fa_bwd",
+                 "fa_bwd_kv", "fa_bwd_strided"):
+        monkeypatch.setattr(binding, name, no_call)
+    monkeypatch.setattr(binding, "fa_fwd_decode_workspace_size", lambda *a: 1024)
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    lse = torch.zeros((1, 1, 8), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        binding.forward(q, q, q)
+    with pytest.raises(ValueError):
+        binding.decode(q, q, q)
+    with pytest.raises(ValueError):
+        binding.backward(q, q, q, q, lse, q)
+
+    # the per-tensor check itself, with a stand-in for a device tensor
+    dev = torch.device("cuda", 0)
+    on_gpu = types.SimpleNamespace(is_cuda=True, device=dev)
+    binding._on_device(dev, out=on_gpu, lse=on_gpu)
+    for bad in (torch.zeros(4), types.SimpleNamespace(is_cuda=True, device=torch.device("cuda", 1))):
+        for name in ("out", "lse", "delta", "workspace", "dq"):
+            with pytest.raises(ValueError, match=name):
+                binding._on_device(dev, **{name: bad})

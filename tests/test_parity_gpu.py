@@ -2,22 +2,20 @@
 
 * small and medium shapes, compared element by element, spanning several
   key and query tiles and ragged tails (S not a multiple of any tile size);
-* the five benchmark workloads at full size, in the same launch the benchmark
-  times: every output checked for finiteness and the value-hull property, one
-  whole head against the oracle, and sampled rows (tile boundaries, first and
-  last rows, random rows) of every head against the oracle one by one;
-* the 24 shapes of the pages' benchmark grid, in the launch the benchmark
-  times: finiteness and sampled rows of 8 heads.
+* the five benchmark workloads and the 24 shapes of the pages' benchmark grid
+  at full size, in the same launch the benchmark times: every output checked
+  for finiteness and the value-hull property, and every element of O and LSE
+  against the oracle;
+* d = 64 causal problems long enough for the ping-pong kernel, in full.
 """
 
-import numpy as np
 import pytest
 import torch
 
 import oracle
 from exact_attention_16_amd.inputs import (SWEEP, SWEEP_BY_NAME, WORKLOADS, WORKLOADS_BY_NAME,
                                            Workload, default_scale, make_inputs)
-from tests.gpu_helpers import TOL_LSE, TOL_O, check_full, gpu_forward, say, to64
+from tests.gpu_helpers import TOL_LSE, TOL_O, check_full, errors, gpu_forward, oracle_workers, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -95,89 +93,56 @@ def test_moving_row_max(shape, d, causal, dtype):
     check_full(q, k, v, causal, default_scale(d), label=f"level {shape}")
 
 
-def test_tiny_workload_full():
-    w = WORKLOADS[0]
-    q, k, v = make_inputs(w)
-    eo, el = check_full(q, k, v, w.causal, default_scale(w.d), label=w.name)
-    print(f"tiny: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
-
-
-def _sample_rows(S, rng, n_random):
-    fixed = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, S // 2, S - 2, S - 1}
-    rows = sorted(r for r in fixed if 0 <= r < S)
-    rows += rng.choice(S, size=min(S, n_random), replace=False).tolist()
-    return rows
-
-
-@pytest.mark.parametrize("name", [w.name for w in WORKLOADS[1:]])
-def test_full_size_workload(name):
-    w = WORKLOADS_BY_NAME[name]
+def _compare_whole(w, label):
+    """Every element of O and LSE of workload ``w``, from the launch the
+    benchmark times, against the oracle on the same inputs."""
     scale = default_scale(w.d)
     q, k, v = make_inputs(w)
-    say(f"workload {name} B={w.B} H={w.H} S={w.S} d={w.d} {w.dtype} causal={w.causal}")
+    say(f"{label} {w.name} B={w.B} H={w.H} S={w.S} d={w.d} {w.dtype} causal={w.causal}")
     o, lse = gpu_forward(q, k, v, w.causal, scale)
 
     # properties over every output: finite; each O_i inside the per-head
-    # coordinatewise range of V (exact attention averages value rows)
+    # coordinatewise range of V (exact attention averages value rows; P is
+    # rounded to the input dtype before the PV product and O to the dtype on
+    # output, hence the margin)
     assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
     vd = v.cuda().float()
     lo = vd.amin(dim=2, keepdim=True)
     hi = vd.amax(dim=2, keepdim=True)
     of = o.float()
-    margin = 0.05  # P is rounded to the input dtype before the PV product
+    margin = 0.05
     assert bool(((of >= lo - margin) & (of <= hi + margin)).all().item())
     del vd, lo, hi, of
 
     o_cpu = o.float().cpu().double().numpy()
     lse_cpu = lse.cpu().double().numpy()
     del o, lse
-    qn, kn, vn = to64(q), to64(k), to64(v)
+    o_ref, lse_ref = oracle.attention(to64(q), to64(k), to64(v), w.causal, scale, workers=oracle_workers())
+    eo, el = errors(o_cpu, lse_cpu, o_ref, lse_ref)
+    print(f"{w.name}: all {o_cpu.size} O and {lse_cpu.size} LSE elements max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE, (w.name, eo, el)
 
-    # one whole head
-    b0, h0 = w.B - 1, w.H // 2
-    oh, lh = oracle.attention_head(qn[b0, h0], kn[b0, h0], vn[b0, h0], w.causal, scale)
-    eo = float(np.abs(o_cpu[b0, h0] - oh).max())
-    el = float(np.abs(lse_cpu[b0, h0] - lh).max())
-    print(f"{name}: whole head ({b0},{h0}) max|dO|={eo:.3e} max|dLSE|={el:.3e}")
-    assert eo <= TOL_O and el <= TOL_LSE, (eo, el)
 
-    # sampled rows of (up to) 64 heads
-    rng = np.random.default_rng(w.seed)
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    if len(heads) > 64:
-        heads = [heads[i] for i in rng.choice(len(heads), size=64, replace=False)]
-    samples = [(b, h, i) for (b, h) in heads for i in _sample_rows(w.S, rng, 24)]
-    so, sl = oracle.attention_samples(qn, kn, vn, w.causal, scale, samples)
-    got_o = np.stack([o_cpu[b, h, i] for (b, h, i) in samples])
-    got_l = np.array([lse_cpu[b, h, i] for (b, h, i) in samples])
-    eo = float(np.abs(got_o - so).max())
-    el = float(np.abs(got_l - sl).max())
-    print(f"{name}: {len(samples)} sampled rows max|dO|={eo:.3e} max|dLSE|={el:.3e}")
-    assert eo <= TOL_O and el <= TOL_LSE, (eo, el)
+@pytest.mark.parametrize("name", [w.name for w in WORKLOADS])
+def test_full_size_workload(name):
+    """The five benchmark workloads at full size, every output element."""
+    _compare_whole(WORKLOADS_BY_NAME[name], "workload")
 
 
 @pytest.mark.parametrize("name", [w.name for w in SWEEP])
-def test_sweep_sampled(name):
+def test_sweep_full(name):
     """The pages' kernel-benchmark grid (S 512..16k x d 64/128 x causal, 16k
-    tokens per batch), in the launch the benchmark times: every output
-    finite, and sampled rows of 8 heads against the oracle one by one."""
-    w = SWEEP_BY_NAME[name]
-    scale = default_scale(w.d)
-    q, k, v = make_inputs(w)
-    say(f"sweep {name} B={w.B} H={w.H} S={w.S} d={w.d} causal={w.causal}")
-    o, lse = gpu_forward(q, k, v, w.causal, scale)
-    assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
-    o_cpu = o.float().cpu().double().numpy()
-    lse_cpu = lse.cpu().double().numpy()
-    del o, lse
-    rng = np.random.default_rng(w.seed)
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    heads = [heads[i] for i in rng.choice(len(heads), size=min(8, len(heads)), replace=False)]
-    samples = [(b, h, i) for (b, h) in heads for i in _sample_rows(w.S, rng, 8)]
-    so, sl = oracle.attention_samples(to64(q), to64(k), to64(v), w.causal, scale, samples)
-    got_o = np.stack([o_cpu[b, h, i] for (b, h, i) in samples])
-    got_l = np.array([lse_cpu[b, h, i] for (b, h, i) in samples])
-    eo = float(np.abs(got_o - so).max())
-    el = float(np.abs(got_l - sl).max())
-    print(f"{name}: {len(samples)} sampled rows max|dO|={eo:.3e} max|dLSE|={el:.3e}")
-    assert eo <= TOL_O and el <= TOL_LSE, (eo, el)
+    tokens per batch), in the launch the benchmark times, every output
+    element.  The grid reaches every forward instantiation at bf16: the
+    ping-pong kernel at d = 64 / 128 with and without the causal mask, and the
+    in-order kernel that short causal problems use."""
+    _compare_whole(SWEEP_BY_NAME[name], "sweep")
+
+
+@pytest.mark.parametrize("B,H,S,dtype", [(1, 2, 4096, "bf16"), (1, 2, 4096, "fp16"), (1, 1, 8192, "fp16"),
+                                         (2, 1, 6144, "bf16")])
+def test_causal_d64_long(B, H, S, dtype):
+    """d = 64 causal problems longer than 2048 keys run the ping-pong kernel
+    (shorter ones the in-order kernel); every element against the oracle."""
+    w = Workload("causal_d64_long", B, H, S, 64, dtype, True, seed=40_000 + S + B)
+    _compare_whole(w, "causal d64")

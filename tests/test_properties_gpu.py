@@ -142,3 +142,28 @@ def test_binding_rejects_bad_arguments():
     with pytest.raises(fa.FaError) as e:
         fa.forward(q, q, q, out=q)
     assert e.value.status == -7
+
+
+def test_binding_rejects_host_outputs_and_scratch():
+    """out, lse, delta, workspace and the gradients must be device tensors:
+    host buffers are rejected before any launch."""
+    say("host outputs rejected")
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    host = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16)
+    host_lse = torch.zeros((1, 1, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="out"):
+        fa.forward(q, q, q, out=host)
+    with pytest.raises(ValueError, match="lse"):
+        fa.forward(q, q, q, lse=host_lse)
+    with pytest.raises(ValueError, match="out"):
+        fa.decode(q, q, q, out=host)
+    with pytest.raises(ValueError, match="workspace"):
+        fa.decode(q, q, q, workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+    o, lse = fa.forward(q, q, q)
+    with pytest.raises(ValueError, match="lse"):
+        fa.backward(q, q, q, o, host_lse, q)
+    with pytest.raises(ValueError, match="delta"):
+        fa.backward(q, q, q, o, lse, q, delta=host_lse)
+    with pytest.raises(ValueError, match="dq"):
+        fa.backward(q, q, q, o, lse, q, dq=host)
+    torch.cuda.synchronize()
