@@ -12,16 +12,20 @@ loaded on first use and its absence is an error.
 from .binding import (  # noqa: F401
     FA_DTYPE_BF16,
     FA_DTYPE_FP16,
+    FA_DECODE_NOALLOC_MAX_BYTES,
+    FA_ERR_SCRATCH,
     FA_ERR_STRIDE,
     FA_ERR_WORKSPACE,
     FaError,
     backward,
     decode,
+    decode_noalloc,
     fa_bwd,
     fa_bwd_kv,
     fa_bwd_strided,
     fa_fwd,
     fa_fwd_decode,
+    fa_fwd_decode_noalloc,
     fa_fwd_decode_strided,
     fa_fwd_decode_workspace_size,
     fa_fwd_kv,

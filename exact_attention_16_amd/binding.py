@@ -21,6 +21,8 @@ FA_OK = 0
 FA_ERR_HIP = -9
 FA_ERR_WORKSPACE = -10
 FA_ERR_STRIDE = -11
+FA_ERR_SCRATCH = -12
+FA_DECODE_NOALLOC_MAX_BYTES = 16 << 20
 
 _DTYPES = {torch.float16: FA_DTYPE_FP16, torch.bfloat16: FA_DTYPE_BF16}
 
@@ -55,6 +57,8 @@ def load_library() -> ctypes.CDLL:
             lib.fa_fwd_decode_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i, f, i, vp,
                                                   ctypes.c_size_t, vp]
             lib.fa_fwd_decode_strided.restype = i
+            lib.fa_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+            lib.fa_fwd_decode_noalloc.restype = i
             lib.fa_fwd_decode_workspace_size.argtypes = [i, i, i, i, i]
             lib.fa_fwd_decode_workspace_size.restype = ctypes.c_size_t
             lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
@@ -102,6 +106,12 @@ def fa_fwd_decode(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, worksp
     """The C entry point with plain integers as pointers; returns the status."""
     return int(load_library().fa_fwd_decode(q, k, v, o, lse, int(B), int(H), int(Sq), int(Sk), int(d), int(causal),
                                              float(scale), int(dtype), workspace, int(workspace_bytes), stream))
+
+
+def fa_fwd_decode_noalloc(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, stream) -> int:
+    """The C entry point with plain integers as pointers; returns the status."""
+    return int(load_library().fa_fwd_decode_noalloc(q, k, v, o, lse, int(B), int(H), int(Sq), int(Sk), int(d),
+                                                     int(causal), float(scale), int(dtype), stream))
 
 
 def _strides_arg(strides):
@@ -292,6 +302,40 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
                                           s.cuda_stream), "fa_fwd_decode_strided"
     if st != FA_OK:
         raise FaError(st, entry)
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                   causal: bool = False, scale: float | None = None, stream: torch.cuda.Stream | None = None):
+    """fa_fwd_decode_noalloc: ``decode`` with the library's own scratch array
+    instead of a workspace, for callers that cannot allocate.  Dense tensors
+    only; ``out`` [B, H, Sq, d] and ``lse`` [B, H, Sq] float32 are the
+    caller's.  Calls that may overlap on one device race on the shared array.
+    Returns (out, lse)."""
+    if (q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[:2] != q.shape[:2]
+            or k.shape[3] != q.shape[3]):
+        raise ValueError(f"need q [B, H, Sq, d] and k, v [B, H, Sk, d], got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise TypeError("q, k, v must all be float16 or all bfloat16")
+    if not q.is_cuda:
+        raise ValueError("q, k, v must be device tensors")
+    _on_device(q.device, k=k, v=v, out=out, lse=lse)
+    B, H, Sq, d = q.shape
+    Sk = k.shape[2]
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be a tensor like q")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, Sq] tensor")
+    if not all(t.is_contiguous() for t in (q, k, v, out, lse)):
+        raise ValueError("fa_fwd_decode_noalloc takes dense (contiguous) tensors")
+    if scale is None:
+        scale = float(torch.tensor(d, dtype=torch.float32).rsqrt())
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = fa_fwd_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Sq,
+                               Sk, d, 1 if causal else 0, scale, _DTYPES[q.dtype], s.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_decode_noalloc")
     return out, lse
 
 

@@ -232,6 +232,32 @@ int decode(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(fa::launch_decode(a, plan, (hipStream_t)stream));
 }
 
+static_assert(FA_DECODE_NOALLOC_MAX_BYTES == fa::kDecodeScratchBytes, "scratch size in fa.h and fa_launch.h");
+
+// fa_fwd_decode with the library's scratch array as the workspace: the same
+// validation (minus the workspace argument), a size check against the array,
+// then the same kernels.
+int decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq, int Sk,
+                   int d, int causal, float scale, int dtype, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * Sq == 0) return FA_OK;
+  fa::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.strides = nullptr;
+  const fa::DecodePlan plan = fa::decode_plan(a);
+  if (plan.grid > 0x7fffffffLL || (long long)B * H * Sq > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+  if (plan.workspace_bytes > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+  hipError_t err = hipSuccess;
+  a.workspace = fa::decode_scratch((hipStream_t)stream, &err);
+  if (!a.workspace) return hip_status(err);
+  return hip_status(fa::launch_decode(a, plan, (hipStream_t)stream));
+}
+
 int backward(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
              void* dk, void* dv, float* delta, int B, int H, int Sq, int Sk, int d, int causal, float scale,
              int dtype, void* stream, const long long* strides, bool strided, bool square) {
@@ -281,6 +307,11 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o, float* l
   return decode(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, workspace, workspace_bytes, stream);
 }
 
+int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
+                          int Sk, int d, int causal, float scale, int dtype, void* stream) {
+  return decode_noalloc(q, k, v, o, lse, B, H, Sq, Sk, d, causal, scale, dtype, stream);
+}
+
 int fa_fwd_decode_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
                           int Sk, int d, const long long* strides, int causal, float scale, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream) {
@@ -327,6 +358,9 @@ const char* fa_status_string(int status) {
              "element";
     case FA_ERR_WORKSPACE:
       return "workspace is NULL, smaller than fa_fwd_decode_workspace_size() or not 16-byte aligned";
+    case FA_ERR_SCRATCH:
+      return "fa_fwd_decode_noalloc: these shapes need more than FA_DECODE_NOALLOC_MAX_BYTES of scratch "
+             "(fa_fwd_decode_workspace_size() bytes); use fa_fwd_decode with a workspace";
     default: return "unknown status";
   }
 }

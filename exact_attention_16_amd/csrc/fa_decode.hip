@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_fwd_wave.h"
 #include "fa_launch.h"
@@ -392,6 +394,55 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   if (a.dtype == 1)
     return launch_decode_dt<__bf16>(a, plan, stream);
   return launch_decode_dt<_Float16>(a, plan, stream);
+}
+
+namespace {
+
+// The partial results of fa_fwd_decode_noalloc.  Host code never uses this
+// name as an address (on the host it is only a stand-in for the symbol):
+// each device's copy is found with hipGetSymbolAddress and that pointer is
+// what the kernels receive.
+__device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+void* decode_scratch(hipStream_t stream, hipError_t* err) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    // with the stream's device current, as the symbol lookup requires
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess || (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)) {
+      *err = e;
+      return nullptr;
+    }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess || !ptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *err = hipSuccess;
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace fa

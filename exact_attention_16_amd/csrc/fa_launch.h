@@ -93,4 +93,14 @@ DecodePlan decode_plan(const DecodeArgs& a);
 // Enqueue the split kernel and the merge kernel on `stream`.
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
+// Bytes of the library-owned scratch array (fa_decode.hip) that
+// fa_fwd_decode_noalloc uses as its workspace; one copy per device.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+
+// Device address of the scratch array's copy on the device that `stream`
+// belongs to (the current device for the NULL stream).  Looked up once per
+// device with hipGetSymbolAddress and kept; allocates nothing.  On failure
+// returns nullptr and sets *err.
+void* decode_scratch(hipStream_t stream, hipError_t* err);
+
 }  // namespace fa

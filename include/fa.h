@@ -47,8 +47,10 @@ enum {
   FA_ERR_TOO_LARGE = -8, /* S*d or Sk*d >= 2^30, or the grid exceeds 2^31-1      */
   FA_ERR_HIP = -9,       /* the HIP runtime rejected the launch (see below)      */
   FA_ERR_WORKSPACE = -10, /* fa_fwd_decode: workspace missing, short or unaligned */
-  FA_ERR_STRIDE = -11    /* strided entry points: a stride negative, a row stride
+  FA_ERR_STRIDE = -11,   /* strided entry points: a stride negative, a row stride
                             below d, or the output's strides not one-to-one   */
+  FA_ERR_SCRATCH = -12   /* fa_fwd_decode_noalloc: the shapes need more than
+                            FA_DECODE_NOALLOC_MAX_BYTES of scratch            */
 };
 
 /*
@@ -184,6 +186,38 @@ int fa_fwd_decode(const void* q, const void* k, const void* v, void* o,
  * a negative size); then fa_fwd_decode needs no workspace or fails validation.
  */
 size_t fa_fwd_decode_workspace_size(int B, int H, int Sq, int Sk, int d);
+
+/*
+ * fa_fwd_decode_noalloc -- fa_fwd_decode for callers that cannot allocate
+ * (code under stream or graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same operation, validation and kernels, but the
+ * partial results live in a library-owned device array of
+ * FA_DECODE_NOALLOC_MAX_BYTES, so the caller passes only q, k, v, o and lse
+ * (dense layout, as for fa_fwd_decode) and no workspace.
+ *
+ * Limit: shapes whose fa_fwd_decode_workspace_size(B, H, Sq, Sk, d) exceeds
+ * FA_DECODE_NOALLOC_MAX_BYTES return FA_ERR_SCRATCH before anything is
+ * enqueued (16 MiB covers, e.g., every single-token step with B*H*d up to
+ * about 4M).
+ *
+ * Memory: each device the library runs this on holds its own copy of the
+ * array until the process ends.  The first call on a device looks up that
+ * copy's address (hipGetSymbolAddress, with the stream's device current);
+ * no call allocates or frees anything.  Nothing in the array needs clearing:
+ * every partial the merge reads is written first by the same call.
+ *
+ * Concurrency: all calls on one device share that device's array.  Calls
+ * ordered on one stream are fine; calls that may overlap on one device
+ * (different streams, different threads without ordering) race on it and
+ * give wrong results.
+ *
+ * Arguments and other errors: as fa_fwd_decode without the workspace
+ * arguments.  Results are bitwise those of fa_fwd_decode on the same inputs.
+ */
+#define FA_DECODE_NOALLOC_MAX_BYTES (16u << 20)
+int fa_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                          float* lse, int B, int H, int Sq, int Sk, int d,
+                          int causal, float scale, int dtype, void* stream);
 
 /*
  * fa_fwd_decode_strided -- fa_fwd_decode on strided tensors (strides and

@@ -29,7 +29,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_kv", "fa_bwd_strided", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_strided",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_kv", "fa_bwd_strided", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_noalloc",
+                                   "fa_fwd_decode_strided",
                                    "fa_fwd_decode_workspace_size", "fa_fwd_kv", "fa_fwd_strided",
                                    "fa_last_hip_error", "fa_status_string", "fa_version"]
 
@@ -385,3 +386,31 @@ def test_binding_rejects_host_tensors_before_any_call(monkeypatch):
         for name in ("out", "lse", "delta", "workspace", "dq"):
             with pytest.raises(ValueError, match=name):
                 binding._on_device(dev, **{name: bad})
+
+
+# fa_fwd_decode_noalloc: fa_fwd_decode's validation without the workspace,
+# then a size check against the library's scratch array -- all before any
+# HIP call.
+def call_noalloc(**kw):
+    a = dict(GOOD_KV)
+    a.update(kw)
+    return fa.fa_fwd_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Sq"], a["Sk"],
+                                    a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(Sk=-1), -2), (dict(d=96), -3), (dict(dtype=9), -4), (dict(scale=-1.0), -5),
+    (dict(o=O + 2), -6), (dict(o=Q), -7),
+])
+def test_noalloc_validation_errors(lib, kw, status):
+    assert call_noalloc(**kw) == status, fa.fa_status_string(status)
+
+
+def test_noalloc_scratch_limit_and_empty_problem(lib):
+    big = dict(B=64, H=64, Sq=64, Sk=2048, d=64)
+    assert fa.fa_fwd_decode_workspace_size(64, 64, 64, 2048, 64) > fa.FA_DECODE_NOALLOC_MAX_BYTES
+    far = {n: BASE + i * (1 << 32) for i, n in enumerate(("q", "k", "v", "o", "lse"))}
+    assert call_noalloc(**big, **far) == fa.FA_ERR_SCRATCH
+    assert "scratch" in fa.fa_status_string(fa.FA_ERR_SCRATCH)
+    for dims in (dict(B=0), dict(H=0), dict(Sq=0)):
+        assert call_noalloc(q=0, k=0, v=0, o=0, lse=0, **dims) == 0
