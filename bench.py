@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-per-config] [--no-parity]
                     [--no-sweep] [--no-backward] [--no-decode] [--no-wide]
-                    [--decode NAMES] [--copy-calibration]
+                    [--decode NAMES] [--backward NAMES] [--copy-calibration]
 
 One step is one exact-attention forward pass (every step of the method, one
 kernel launch) over one batch of the workload's synthetic inputs, already
@@ -332,6 +332,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the split-key decoding timings")
     ap.add_argument("--no-wide", action="store_true", help="skip the wide-head (d = 192, 256) timings")
     ap.add_argument("--decode", default="", help="comma-separated decoding workloads (default: all)")
+    ap.add_argument("--backward", default="", help="comma-separated workloads for the gradient timings (default: all)")
     ap.add_argument("--cpu-heads", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -356,7 +357,10 @@ def main():
         print(json.dumps(copy_calibration(args.steps)), flush=True)
         return
 
-    w = WORKLOADS_BY_NAME[args.workload]
+    # the headline workload: one of the five, or any shape of the grid or the
+    # wide heads (for profiling a single kernel instantiation)
+    every = {**WORKLOADS_BY_NAME, **{x.name: x for x in SWEEP + WIDE}}
+    w = every[args.workload]
     torch.cuda.synchronize()
     r = time_workload(w, args.steps, args.warmup, per_launch=True)
     torch.cuda.synchronize()
@@ -369,7 +373,8 @@ def main():
     roof["algorithmic_bytes"] = algorithmic_bytes(w)
     roof["flops"] = f
     roof["mfma_frac"] = value / PEAK_MFMA_TFLOPS
-    roof["kernel"] = "fa::detail::fwd_kernel"
+    in_order = w.d > 128 or (w.causal and w.S <= (2048 if w.d == 64 else 1024))
+    roof["kernel"] = "fa::detail::fwd_wide_kernel" if in_order else "fa::detail::fwd_kernel"
     roof["launch_ms"] = ms
     roof["launch_stats"] = r["launch_stats"]
 
@@ -390,7 +395,10 @@ def main():
     # more, which the count does not credit.
     backward = {}
     if not args.no_backward:
+        only = [n for n in args.backward.split(",") if n]
         for wc in WORKLOADS + (() if args.no_wide else WIDE):
+            if only and wc.name not in only:
+                continue
             steps = max(5, min(args.steps, int(2e9 / max(1.0, 2.5 * flops(wc) / 1e3))))
             rb = time_backward(wc, steps, args.warmup)
             msb = rb["total_ms"] / steps

@@ -81,6 +81,7 @@ struct Params {
   int Sk;      // key rows per head (= S for self-attention)
   int shift;   // causal offset: query row i sits at key position i + shift (Sk - S)
   int nqb;     // query-row blocks per head
+  int persist; // 1: persistent grid, each work-group walks its own list of query blocks
   float c;     // scale * log2(e): scores enter exp2 as c * s
   // Strided layouts only: heads per batch entry, the batch and head strides
   // (elements) of q, k, v, o, and their row strides (bytes).

@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_fwd_wave.h"
 #include "fa_launch.h"
@@ -96,48 +98,82 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
   w.col = w.lane & 31;
   const int group = w.wave >> 2;
 
+  // One query block per work-group, or (persistent grid) the work-group's
+  // list of blocks one after the other.
+  // (only causal instantiations at d = 128 are launched persistent; the
+  // others keep the one-block code)
+  constexpr bool kPersist = CAUSAL && D == 128;
+  BlockCursor<CAUSAL> cur;
   int bh, qb;
-  map_query_block<CAUSAL>(blockIdx.x, p.BH, p.nqb, bh, qb);
-  const int q_lo = qb * W::BM;
-  // Row blocks alternate between the groups (group 0: blocks 0, 2, 4, 6;
-  // group 1: 1, 3, 5, 7), so near the causal diagonal both groups still have
-  // about the same number of key tiles and neither idles beside the other.
-  w.qw = q_lo + 32 * (2 * (w.wave & 3) + group);
-  w.myq = w.qw + w.col;
-  const size_t head_elems = w.setup(p, bh);
-
-  // keys this work-group visits (causal: up to its last row's position)
-  const int kv_end = CAUSAL ? min(p.Sk, q_lo + W::BM + p.shift) : p.Sk;
-  const int n = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-  w.n = n;
-
-  w.issue_k(0, k_lds0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  barrier();
-
-  for (int k = 0; k <= n; k += 2) {
-    // ---- even k: K_k in buffer 0, V_{k-1} in buffer 1
-    if (k + 1 < n) w.issue_k(k + 1, k_lds1);
-    if (k < n) w.issue_v(k, v_lds0);
-    if (group == 0) w.mfma_phase(k, k_lds0, v_lds1); else w.soft_phase(k - 1);
-    barrier();
-    if (group == 0) w.soft_phase(k); else w.mfma_phase(k, k_lds0, v_lds1);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    barrier();
-    if (k + 1 > n) break;
-    // ---- odd k+1: K_{k+1} in buffer 1, V_k in buffer 0
-    if (k + 2 < n) w.issue_k(k + 2, k_lds0);
-    if (k + 1 < n) w.issue_v(k + 1, v_lds1);
-    if (group == 0) w.mfma_phase(k + 1, k_lds1, v_lds0); else w.soft_phase(k);
-    barrier();
-    if (group == 0) w.soft_phase(k + 1); else w.mfma_phase(k + 1, k_lds1, v_lds0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    barrier();
+  bool more;
+  if (kPersist && p.persist) {
+    cur.init(p);
+    more = cur.next(p, bh, qb);
+  } else {
+    map_query_block<CAUSAL>(blockIdx.x, p.BH, p.nqb, bh, qb);
+    more = true;
   }
-  w.store(p.o, p.lse, head_elems, bh);
+  while (more) {
+    const int q_lo = qb * W::BM;
+    // Row blocks alternate between the groups (group 0: blocks 0, 2, 4, 6;
+    // group 1: 1, 3, 5, 7), so near the causal diagonal both groups still
+    // have about the same number of key tiles and neither idles beside the
+    // other.
+    w.qw = q_lo + 32 * (2 * (w.wave & 3) + group);
+    w.myq = w.qw + w.col;
+    const size_t head_elems = w.setup(p, bh);
+
+    // keys this work-group visits (causal: up to its last row's position)
+    const int kv_end = CAUSAL ? min(p.Sk, q_lo + W::BM + p.shift) : p.Sk;
+    const int n = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+    w.n = n;
+
+    w.issue_k(0, k_lds0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    barrier();
+
+    for (int k = 0; k <= n; k += 2) {
+      // ---- even k: K_k in buffer 0, V_{k-1} in buffer 1
+      if (k + 1 < n) w.issue_k(k + 1, k_lds1);
+      if (k < n) w.issue_v(k, v_lds0);
+      if (group == 0) w.mfma_phase(k, k_lds0, v_lds1); else w.soft_phase(k - 1);
+      barrier();
+      if (group == 0) w.soft_phase(k); else w.mfma_phase(k, k_lds0, v_lds1);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      barrier();
+      if (k + 1 > n) break;
+      // ---- odd k+1: K_{k+1} in buffer 1, V_k in buffer 0
+      if (k + 2 < n) w.issue_k(k + 2, k_lds0);
+      if (k + 1 < n) w.issue_v(k + 1, v_lds1);
+      if (group == 0) w.mfma_phase(k + 1, k_lds1, v_lds0); else w.soft_phase(k);
+      barrier();
+      if (group == 0) w.soft_phase(k + 1); else w.mfma_phase(k + 1, k_lds1, v_lds0);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      barrier();
+    }
+    // (every LDS read of this block happened before the last barrier, so the
+    // next block's first K tile may overwrite the buffers)
+    w.store(p.o, p.lse, head_elems, bh);
+    more = (kPersist && p.persist) ? cur.next(p, bh, qb) : false;
+  }
 }
 
 constexpr int kWaves = 8;
+
+// Compute units of the device `stream` runs on (the current device for the
+// NULL stream), looked up once per device; 0 if the runtime cannot say.
+int device_cus(hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 ||
+      dev >= kMaxDevices)
+    return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    cache[dev].store(n, std::memory_order_relaxed);
+  return n > 0 ? n : 0;
+}
 // Keys per tile (chosen by measurement on the MI355X).
 template <int D>
 constexpr int key_tile() { return 64; }
@@ -167,7 +203,22 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     p.vsb = st[6]; p.vsh = st[7]; p.v_rs = (uint32_t)(st[8] * 2);
     p.osb = st[9]; p.osh = st[10]; p.o_rs = (uint32_t)(st[11] * 2);
   }
-  const long long grid = (long long)p.nqb * p.BH;
+  long long grid = (long long)p.nqb * p.BH;
+  // Causal problems at d = 128 run a persistent grid: one work-group per
+  // compute unit, each working through its list of (long, short) query-block
+  // pairs, so every work-group gets the same number of key tiles (see
+  // BlockCursor).  (At d = 64 the loop cost registers, spills and 15-18 %
+  // at S >= 4096 on the MI355X, so d = 64 keeps one block per work-group.)
+  p.persist = 0;
+  if (D == 128 && a.causal) {
+    // resident work-groups: (waves per SIMD x 4 SIMDs) / kWaves per compute unit
+    const long long slots = (long long)device_cus(stream) * (waves_per_simd<D, CAUSAL, TAIL>() * 4 / kWaves);
+    const long long units = (long long)p.BH * ((p.nqb + 1) / 2);
+    if (slots > 0 && units > slots) {
+      p.persist = 1;
+      grid = slots;
+    }
+  }
   hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, key_tile<D>(), STRIDED>), dim3((unsigned)grid),
                      dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();

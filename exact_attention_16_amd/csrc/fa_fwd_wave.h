@@ -41,6 +41,67 @@ __device__ __forceinline__ void map_query_block(unsigned id, int BH, int nqb, in
   if (CAUSAL) qb = nqb - 1 - qb;
 }
 
+// The query blocks one work-group of a persistent grid works through.
+// Units are dealt to the work-groups of each XCD (work-group i runs on XCD
+// i % kXcds): with B*H a multiple of kXcds, XCD x owns heads x, x + kXcds,
+// ... and its work-groups take that list's units in turn, so the work-groups
+// of an XCD work on the same few heads at a time and share their K/V tiles
+// in the XCD's L2.  A causal unit is the pair of query blocks (nqb-1-u, u)
+// of one head: nqb + 1 row blocks' worth of key tiles for every pair, so the
+// work-groups finish together whatever the head length (one block alone in
+// the middle when nqb is odd).  A non-causal unit is one query block.
+template <bool CAUSAL>
+struct BlockCursor {
+  int u, stride, units, xcd, upe;
+  bool xcd_map;
+  int part;  // causal: 0 = the long block of the pair, 1 = the short one
+
+  __device__ __forceinline__ void init(const Params& p) {
+    const int G = gridDim.x;
+    upe = CAUSAL ? (p.nqb + 1) / 2 : p.nqb;  // units per head
+    xcd_map = (p.BH % kXcds == 0) && (G % kXcds == 0);
+    if (xcd_map) {
+      xcd = blockIdx.x % kXcds;
+      u = blockIdx.x / kXcds;
+      stride = G / kXcds;
+      units = (p.BH / kXcds) * upe;
+    } else {
+      xcd = 0;
+      u = blockIdx.x;
+      stride = G;
+      units = p.BH * upe;
+    }
+    part = 0;
+  }
+
+  // The next query block of this work-group, or false when none is left.
+  __device__ __forceinline__ bool next(const Params& p, int& bh, int& qb) {
+    while (u < units) {
+      const int head = u / upe, unit = u % upe;
+      bh = xcd_map ? head * kXcds + xcd : head;
+      if (!CAUSAL) {
+        qb = unit;
+        u += stride;
+        return true;
+      }
+      if (part == 0) {
+        qb = p.nqb - 1 - unit;
+        part = 1;
+        if (qb == unit) {  // the middle block of an odd count: alone
+          part = 0;
+          u += stride;
+        }
+        return true;
+      }
+      qb = unit;
+      part = 0;
+      u += stride;
+      return true;
+    }
+    return false;
+  }
+};
+
 // One wavefront's share of a work-group: 32 query rows of one (batch, head),
 // their Q fragments, running statistics and output accumulator, plus the
 // score tile / weights of the key tile in flight.  The work-group's NW

@@ -124,6 +124,7 @@ hipError_t launch_wide_t(const FwdArgs& a, hipStream_t stream) {
   p.Sk = a.Sk;
   p.shift = a.causal ? a.Sk - a.S : a.Sk;  // non-causal wide heads: every key kept
   p.nqb = (a.S + BM - 1) / BM;
+  p.persist = 0;
   p.c = a.scale * 1.4426950408889634f;
   p.H = a.H;
   if (STRIDED) {
