@@ -24,8 +24,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kRsrcWord3 = 0x00020000;
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
-// The partial output is rescaled only when a row max grows by more than this
-// many binary orders of magnitude, so unnormalised weights stay <= 2^8.
+// When the row max is taken (a tile's first visit of a row, or a tile whose
+// weights exceed Elem<T>::kTileSumLimit), the partial output is rescaled only
+// if the max grew by more than this many binary orders of magnitude.
 constexpr float kRescaleMargin = 8.0f;
 // XCDs (each with its own L2) that work-groups are dealt to round-robin.
 constexpr int kXcds = 8;
@@ -48,6 +49,14 @@ struct Elem<__bf16> {
   // packed pair, one v_dot2): a weight's rounding error then cancels between
   // numerator and denominator instead of scaling the whole output row.
   static constexpr bool kRoundedSum = true;
+  // A tile's weights are accepted without the row max while no lane's share
+  // of the tile's row sum (32 weights) exceeds this (FwdWave::softmax_impl).
+  // bf16 weights have fp32's exponent range, so only the fp32 output
+  // accumulator bounds them: with weights up to 2^40, a million keys times
+  // |V| up to 2^64 still fit.  (At least twice 32 * 2^kRescaleMargin, the
+  // largest share a tile can have right after a rescale, so a retried tile
+  // always passes.)
+  static constexpr float kTileSumLimit = 1099511627776.0f;  // 2^40
   static __device__ __forceinline__ float add_packed(unsigned w, float acc) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
@@ -67,6 +76,9 @@ struct Elem<_Float16> {
   // fp16 weights keep 11 significant bits: the exact fp32 row sum serves both
   // the output and the logsumexp.
   static constexpr bool kRoundedSum = false;
+  // fp16 weights must stay below 65504: 2^14 bounds every weight of a share
+  // (and is at least twice 32 * 2^kRescaleMargin, see the bf16 case).
+  static constexpr float kTileSumLimit = 16384.0f;
   static __device__ __forceinline__ float add_packed(unsigned, float acc) { return acc; }
 };
 

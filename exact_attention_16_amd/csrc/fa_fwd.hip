@@ -78,10 +78,12 @@ namespace detail {
 template <int D, bool CAUSAL, bool TAIL>
 constexpr int waves_per_simd() { return D == 64 ? 4 : 2; }
 
-template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN, bool STRIDED>
+// FAST: unmasked tiles take the softmax without the row max when the weights'
+// range allows (FwdWave::softmax_impl).
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN, bool STRIDED, bool FAST>
 __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void fwd_kernel(Params p) {
   static_assert(NW == 8, "the ping-pong schedule pairs wavefronts w and w+4 on one SIMD");
-  using W = FwdWave<T, D, CAUSAL, TAIL, NW, BN, STRIDED>;
+  using W = FwdWave<T, D, CAUSAL, TAIL, NW, BN, STRIDED, FAST>;
   // K and V double buffers as four distinct LDS objects; the step loop is
   // unrolled by two so each access names its buffer at compile time, which
   // lets the compiler see that reads of one buffer never alias the
@@ -219,8 +221,20 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
       grid = slots;
     }
   }
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, key_tile<D>(), STRIDED>), dim3((unsigned)grid),
-                     dim3(kWaves * 64), 0, stream, p);
+  // The fast softmax keeps each tile's scores live while it computes the
+  // weights (for a possible retry): at d = 128 that fits the registers
+  // except in the non-causal ragged variant.  At d = 64 it costs spilled
+  // registers in the step loop, which long non-causal rows repay (S = 2048:
+  // +2-4 %, S = 16384: +5-6 % on the MI355X) and short or causal ones do not
+  // (S = 512: -2 to -7 %, causal S = 4096: -17 %).
+  constexpr bool kFastOk = D == 128 ? (CAUSAL || !TAIL) : !CAUSAL;
+  const bool fast = kFastOk && (D == 128 || a.Sk >= 2048);
+  if (fast)
+    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, key_tile<D>(), STRIDED, kFastOk>),
+                       dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, TAIL, kWaves, key_tile<D>(), STRIDED, false>),
+                       dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

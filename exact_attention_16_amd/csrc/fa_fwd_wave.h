@@ -110,7 +110,7 @@ struct BlockCursor {
 // Rows of a head are ROW_BYTES apart (dense [B][H][S][d] tensors), or, when
 // STRIDED, q_rs / k_rs / v_rs / o_rs bytes apart (e.g. a [B][S][H][d]
 // layout); the head bases and range sizes are set by the kernel either way.
-template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN, bool STRIDED = false>
+template <typename T, int D, bool CAUSAL, bool TAIL, int NW, int BN, bool STRIDED = false, bool FAST = false>
 struct FwdWave {
   static constexpr int BM = NW * 32;
   static constexpr int ROW_BYTES = D * 2;
@@ -316,12 +316,17 @@ struct FwdWave {
     }
   }
 
+  // Does the tile starting at k0 cross the causal diagonal or the sequence end?
+  __device__ __forceinline__ bool tile_masked(int k0) const {
+    return (CAUSAL && k0 + BN - 1 > qw + shift) || (TAIL && k0 + BN > Sk);
+  }
+
   // Online-softmax update for the tile starting at k0 (scores in sacc):
   // mask, row max, lazy rescale of O and l, weights P packed to T.  Only tiles
   // that cross the causal diagonal or the sequence end are MASKED; the two
   // variants are separate instantiations so the selects never run elsewhere.
   __device__ __forceinline__ void softmax(int k0) {
-    if ((CAUSAL && k0 + BN - 1 > qw + shift) || (TAIL && k0 + BN > Sk))
+    if (tile_masked(k0))
       softmax_impl<true>(k0);
     else
       softmax_impl<false>(k0);
@@ -345,6 +350,46 @@ struct FwdWave {
         }
     }
 
+    // The row max only guards the weights' range (after the rescale below
+    // every weight is at most 2^kRescaleMargin).  The weights are first taken
+    // against the current reference without the max, and accepted when every
+    // lane's share of the tile's row sum stays within the dtype's
+    // kTileSumLimit; otherwise (a score grew too far past the reference, or
+    // the row has none yet) the max and rescale run and the weights are taken
+    // again.  The reference may thus trail the row max: weights above 1 are
+    // exact in floating point, and the LSE adds log2 of the larger sum.
+    // (Masked tiles, on the diagonal or at the sequence end, are few: they
+    // always take the max first, which keeps their register use down.)
+    float ts, to;
+    if constexpr (MASKED || !FAST) {
+      rescale_to_max<false>();
+      weights<MASKED>(ts, to);
+    } else {
+      bool slow = __builtin_amdgcn_ballot_w64(m_used == -__builtin_inff()) != 0;
+      while (true) {
+        if (slow) rescale_to_max<true>();
+        weights<MASKED>(ts, to);
+        if (slow || __builtin_amdgcn_ballot_w64(!(ts <= Elem<T>::kTileSumLimit)) == 0) break;
+        slow = true;
+      }
+    }
+    lsum += ts;
+    if constexpr (Elem<T>::kRoundedSum) lsum_o += to;
+  }
+
+  // Row max of the tile in sacc; when it exceeds the reference m_used by more
+  // than kRescaleMargin binary orders (or the row had none), it becomes the
+  // new reference and O and the sums are rescaled to it.
+  template <bool RETRY>
+  __device__ __forceinline__ void rescale_to_max() {
+    // (in the fast path's retry loop, empty asm statements keep the compiler
+    // from hoisting the max out of the loop, where it would run on every tile)
+    if constexpr (RETRY) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(sacc[sb][r]));
+    }
     // row max as a tree (independent max3 chains, then combined)
     float mq[4];
 #pragma unroll
@@ -370,41 +415,117 @@ struct FwdWave {
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
+  }
 
-    // weights; the row sum is kept in four partial sums (independent chains),
-    // the bf16 sum of the rounded weights in two
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+  // The weights of 32-key block sb of the tile against the reference mc,
+  // packed to T into out (the block's two P V operands); adds this lane's
+  // shares of the row sum to ls (four partial sums, independent chains;
+  // `first` starts them) and, for bf16, of the sum of the rounded weights to
+  // lo (two partial sums).
+  template <bool MASKED>
+  __device__ __forceinline__ void weights_block(int sb, float (&ls)[4], float (&lo)[2], bool first,
+                                                i16x8 (&out)[2]) {
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][r], c, -mc));
+      if (MASKED) e[r] = (sacc[sb][r] == -__builtin_inff()) ? 0.f : e[r];
+      ls[r & 3] = (first && r < 4) ? e[r] : ls[r & 3] + e[r];
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned x = Elem<T>::pack(e[8 * cc + 2 * i], e[8 * cc + 2 * i + 1]);
+        w[i] = x;
+        if constexpr (Elem<T>::kRoundedSum) lo[i & 1] = Elem<T>::add_packed(x, lo[i & 1]);
+      }
+      out[cc] = __builtin_bit_cast(i16x8, w);
+    }
+  }
+
+  // The whole tile's weights (into pf); ts returns this lane's share of the
+  // tile's row sum, to (bf16) its share of the sum of the rounded weights.
+  template <bool MASKED>
+  __device__ __forceinline__ void weights(float& ts, float& to) {
+    float ls[4];
     float lo[2] = {0.f, 0.f};
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sb][r], c, -mc));
-        if (MASKED) e[r] = (sacc[sb][r] == -__builtin_inff()) ? 0.f : e[r];
-        ls[r & 3] += e[r];
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        u32x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const unsigned x = Elem<T>::pack(e[8 * cc + 2 * i], e[8 * cc + 2 * i + 1]);
-          w[i] = x;
-          if constexpr (Elem<T>::kRoundedSum) lo[i & 1] = Elem<T>::add_packed(x, lo[i & 1]);
-        }
-        pf[sb][cc] = __builtin_bit_cast(i16x8, w);
-      }
+    for (int sb = 0; sb < SB; ++sb) weights_block<MASKED>(sb, ls, lo, sb == 0, pf[sb]);
+    ts = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    to = lo[0] + lo[1];
+  }
+
+  // Both products of one MFMA phase as a single software pipeline.  MFMA i
+  // (i < NPV: O^T += V^T P^T, d-blocks innermost so that neighbours write
+  // different accumulators; then K Q^T, k-steps outermost) takes its A
+  // operand from LDS, and that fragment is read kAhead MFMAs before it is
+  // used.  Scheduling groups (LDS reads, then one MFMA and the reads of the
+  // fragment kAhead further on, ...) pin this order, so the LDS latency is
+  // covered by the matrix core's work except once at the start.
+  static constexpr int NPV = DB * SB * 2;
+  static constexpr int NQK = KSTEPS * SB;
+  // Only the causal d = 128 variants: elsewhere the deeper read-ahead spilled
+  // registers in the step loop and measured slower on the MI355X.
+  static constexpr int kAhead = (D == 128 && CAUSAL) ? 6 : 0;
+  static constexpr int kGroupMfma = 0x008, kGroupDsRead = 0x100;  // sched_group_barrier masks
+
+  __device__ __forceinline__ i16x8 op_frag(int i, const char* ks, const char* vs) const {
+    if (i < NPV) {
+      const int db = i % DB, sc = i / DB;
+      return v_frag(vs, db, sc >> 1, sc & 1);
     }
-    lsum += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    if constexpr (Elem<T>::kRoundedSum) lsum_o += lo[0] + lo[1];
+    const int j = i - NPV;
+    return k_frag(ks, j % SB, j / SB);
+  }
+
+  __device__ __forceinline__ void op_mfma(int i, i16x8 a) {
+    if (i < NPV) {
+      const int db = i % DB, sc = i / DB;
+      oacc[db] = Elem<T>::mma(a, pf[sc >> 1][sc & 1], oacc[db]);
+    } else {
+      const int j = i - NPV, sb = j % SB, kk = j / SB;
+      sacc[sb] = Elem<T>::mma(a, qf[kk], kk == 0 ? f32x16{} : sacc[sb]);
+    }
+  }
+
+  // LDS reads of fragment i: two transposing 8-byte reads for V^T, one
+  // 16-byte read for K
+  __device__ __forceinline__ static void group_reads(int i) {
+    if (i < NPV)
+      __builtin_amdgcn_sched_group_barrier(kGroupDsRead, 2, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(kGroupDsRead, 1, 0);
+  }
+
+  __device__ __forceinline__ void pv_scores(const char* ks, const char* vs) {
+    constexpr int N = NPV + NQK;
+    i16x8 f[N];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) f[i] = op_frag(i, ks, vs);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) group_reads(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i + kAhead < N) f[i + kAhead] = op_frag(i + kAhead, ks, vs);
+      op_mfma(i, f[i]);
+      __builtin_amdgcn_sched_group_barrier(kGroupMfma, 1, 0);
+      if (i + kAhead < N) group_reads(i + kAhead);
+    }
   }
 
   // Phase MFMA(k): P_{k-1} V_{k-1} (V from vp) and K_k Q^T (K from kc).
   __device__ __forceinline__ void mfma_phase(int k, const char* kc, const char* vp) {
     __builtin_amdgcn_s_setprio(1);
-    if (k >= 1 && active((k - 1) * BN)) pv(vp);
-    if (k < n && active(k * BN)) scores(kc);
+    const bool do_pv = k >= 1 && active((k - 1) * BN);
+    const bool do_qk = k < n && active(k * BN);
+    if (kAhead > 0 && do_pv && do_qk) {
+      pv_scores(kc, vp);
+    } else {
+      if (do_pv) pv(vp);
+      if (do_qk) scores(kc);
+    }
     __builtin_amdgcn_s_setprio(0);
   }
 
