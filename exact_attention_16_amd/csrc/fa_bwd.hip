@@ -30,6 +30,8 @@
 //   wavefront walks the query tiles: S = Q K^T and dP = dO V^T (each lane holds
 //   one key; LSE and D of the tile's queries come from LDS), then
 //   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+//   At d = 128, dkdv16_kernel does the same with 16 keys per wavefront on
+//   16x16x32 MFMAs, so that two wavefronts share each SIMD.
 // Tiles move HBM -> LDS with direct-to-LDS buffer loads in the same
 // fragment-major layouts as the forward kernel, double-buffered.
 
@@ -605,6 +607,296 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
   store_row<T, D>(w.dv, 1.0f, (char*)dvv.base, dvv.bytes, w.myk, w.h, dvv.rs);
 }
 
+// ------------------------------------------ dK/dV kernel, 16 keys per wavefront
+
+// At d = 128 the 32-key wavefront above holds 128 accumulator registers for
+// dK and dV alone and needs more than half of a SIMD's register file, so a
+// SIMD runs one wavefront and its exp / dS work never overlaps matrix work.
+// This variant gives each wavefront 16 keys on v_mfma_f32_16x16x32: half the
+// accumulators, two wavefronts per SIMD, for twice the LDS operand bytes per
+// FLOP.
+//
+// Lane layouts (checked on the MI355X with an in-bounds probe):
+//   v_mfma_f32_16x16x32: A (16 x 32) lane l holds row l%16, k = 8 (l/16) ..
+//     +8; B (32 x 16) lane l holds column l%16, the same k; C (16 x 16) lane l
+//     holds column l%16, rows 4 (l/16) .. +4.
+//   ds_read_b64_tr_b16: in each group of 16 lanes, lane u receives element
+//     u%4 of the 4-element reads of lanes 4 j + u/4, j = 0..3 (the group's
+//     reads as a 4 x 16 block, transposed).
+
+// Tiles of ROWS rows x D columns in two LDS layouts:
+//   A16 layout: 1 KiB block (rb, kk) holds, at lane l, row 16 rb + l%16,
+//     columns 32 kk + 8 (l/16) .. +8: the A operand of a 16x16x32 MFMA whose
+//     m index is the row and whose k index is the column;
+//   T16 layout: block (rb, dp) holds two 512-byte halves x, one per 16-column
+//     d-block 2 dp + x; in a half, the 8 bytes at lane L are row
+//     16 rb + 4 (L/16) + (L%16)/4, columns 16 (2 dp + x) + 4 (L%4) .. +4.
+//     Two transposing reads (rb = 2 ch, 2 ch + 1) then give lane l the A
+//     operand with m = column 16 db + l%16 and k = rows 32 ch +
+//     {4 (l/16) .. +4, 16 + 4 (l/16) .. +4}: the order in which pack16 puts
+//     two C-layout tiles into one B operand.
+template <int D, int NW, int ROWS>
+struct Tile16 {
+  static constexpr int KS = D / 32;
+  static constexpr int BYTES = ROWS * D * 2;
+  static constexpr int LOADS = BYTES / (NW * 1024);
+  static_assert(ROWS % 32 == 0 && LOADS * NW * 1024 == BYTES, "tile must split evenly over wavefronts");
+
+  static __device__ __forceinline__ void issue_a(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
+                                                 int lane, uint32_t rs) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int f = i * NW + wave;  // block (rb, kk)
+      const int rb = f / KS, kk = f % KS;
+      const uint32_t off = base + (uint32_t)(rb * 16 + (lane & 15)) * rs + (kk * 32 + (lane >> 4) * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + f * 1024), 16, off, 0, 0, 0);
+    }
+  }
+
+  // Each lane fetches the 16 bytes that belong at its 16-byte slot: the two
+  // 8-byte reads 2 (l%32), 2 (l%32) + 1 of half l/32.
+  static __device__ __forceinline__ void issue_t(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
+                                                 int lane, uint32_t rs) {
+    const int x = lane >> 5, lp = lane & 31;
+    const int row = 4 * (lp >> 3) + ((lp & 7) >> 1);
+    const int col = x * 16 + (lp & 1) * 8;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int f = i * NW + wave;  // block (rb, dp)
+      const int rb = f / KS, dp = f % KS;
+      const uint32_t off = base + (uint32_t)(rb * 16 + row) * rs + (dp * 32 + col) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + f * 1024), 16, off, 0, 0, 0);
+    }
+  }
+
+  static __device__ __forceinline__ i16x8 frag_a(const char* t, int rb, int kk, int lane) {
+    return *(const i16x8*)(t + (rb * KS + kk) * 1024 + lane * 16);
+  }
+
+  static __device__ __forceinline__ i16x8 frag_t(const char* t, int db, int ch, int lane) {
+    i16x4 half[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int blk = (2 * ch + tt) * KS + (db >> 1);
+      half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + blk * 1024 + (db & 1) * 512 + lane * 8));
+    }
+    return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
+// Two C-layout 16x16 tiles (4 values per lane each: rows 4 (l/16) + t) as one
+// B operand whose k index runs over their 32 rows in the order frag_t reads.
+template <typename T>
+__device__ __forceinline__ i16x8 pack16(const float (&e)[8]) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = Elem<T>::pack(e[2 * i], e[2 * i + 1]);
+  return __builtin_bit_cast(i16x8, w);
+}
+
+template <typename T, int D, bool CAUSAL, int NW, int BQ>
+struct Dkv16Wave {
+  using QT = Tile16<D, NW, BQ>;
+  static constexpr int KS = D / 32;
+  static constexpr int DB = D / 16;   // 16-column d-blocks of dK, dV
+  static constexpr int QB = BQ / 16;  // 16-query blocks of S, dP
+  static constexpr int NCH = BQ / 32; // 32-query chunks of the dV, dK products
+
+  int lane, g, kw, myk, shift;
+  float c;
+  i16x8 kf[KS], vf[KS];
+  f32x4 dk[DB], dv[DB];
+
+  __device__ __forceinline__ bool active(int q0) const { return !(CAUSAL && q0 + BQ - 1 + shift < kw); }
+  __device__ __forceinline__ bool masked(int q0) const { return CAUSAL && q0 + shift < kw + 15; }
+
+  // One query tile: qA, dA = Q, dO (A16 layout); qT, dT = Q, dO (T16
+  // layout); st = the tile's LSE in log2 units (floats 0..BQ-1), then D.
+  template <bool MASKED>
+  __device__ __forceinline__ void step(const char* qA, const char* dA, const char* qT, const char* dT,
+                                       const float* st, int q0) {
+    f32x4 s[QB], dp[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb] = dp[qb] = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s[qb] = Elem<T>::mma16(QT::frag_a(qA, qb, kk, lane), kf[kk], s[qb]);
+        dp[qb] = Elem<T>::mma16(QT::frag_a(dA, qb, kk, lane), vf[kk], dp[qb]);
+      }
+    i16x8 pf[NCH], dsf[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      float pe[8], de[8];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int qb = 2 * ch + tt;
+        // queries 16 qb + 4 g + (0..3)
+        const int qi = qb * 16 + 4 * g;
+        const float4 l4 = *(const float4*)(st + qi);
+        const float4 d4 = *(const float4*)(st + BQ + qi);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][t], c, -lv[t]));
+          // a select: a row that keeps no key has LSE = -inf and p = +inf
+          if (MASKED) p = (q0 + qi + t + shift >= myk) ? p : 0.f;
+          pe[4 * tt + t] = p;
+          de[4 * tt + t] = p * (dp[qb][t] - dl[t]);
+        }
+      }
+      pf[ch] = pack16<T>(pe);
+      dsf[ch] = pack16<T>(de);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        dv[db] = Elem<T>::mma16(QT::frag_t(dT, db, ch, lane), pf[ch], dv[db]);
+        dk[db] = Elem<T>::mma16(QT::frag_t(qT, db, ch, lane), dsf[ch], dk[db]);
+      }
+  }
+};
+
+// The lane's key row as the B operand of S = Q K^T (k = column): columns
+// 32 kk + 8 g .. +8; rows past the range read 0.
+template <int D>
+__device__ __forceinline__ void load_row_frags16(i16x8 (&f)[D / 32], const View& v, int row, int g) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(v.base, v.bytes);
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const uint32_t off = (uint32_t)row * v.rs + (kk * 32 + g * 8) * 2;
+    f[kk] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+}
+
+// A C-layout accumulator set (acc[db] holds columns 16 db + 4 g .. +4 of the
+// lane's row) times `mul`, stored as that row of a row-major tensor in T.
+template <typename T, int D>
+__device__ __forceinline__ void store_row16(const f32x4 (&acc)[D / 16], float mul, const View& v, int row, int g) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(v.base, v.bytes);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) {
+    u32x2 w;
+    w[0] = Elem<T>::pack(acc[db][0] * mul, acc[db][1] * mul);
+    w[1] = Elem<T>::pack(acc[db][2] * mul, acc[db][3] * mul);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, (uint32_t)row * v.rs + (db * 16 + 4 * g) * 2, 0, 0);
+  }
+}
+
+// LSE (times log2 e) and D of a query tile: wavefront 0 loads the LSE values,
+// wavefront 1 the D values, one per lane (rows past the sequence read 0);
+// put_stats16 writes them to LDS once the loads have landed.
+template <int BQ>
+__device__ __forceinline__ float load_stats16(__amdgpu_buffer_rsrc_t rl, __amdgpu_buffer_rsrc_t rd, int q0, int wave,
+                                              int lane) {
+  static_assert(BQ <= 64, "one value per lane");
+  const uint32_t off = (lane < BQ) ? (uint32_t)(q0 + lane) * 4 : 0x7FFFFFF0u;
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wave == 0 ? rl : rd, off, 0, 0));
+}
+
+template <int BQ>
+__device__ __forceinline__ void put_stats16(float* st, float v, int wave, int lane) {
+  if (wave < 2 && lane < BQ) st[wave * BQ + lane] = wave == 0 ? v * kLog2e : v;
+}
+
+template <typename T, int D, bool CAUSAL, int NW, int BQ, bool STRIDED>
+__global__ __launch_bounds__(NW * 64, 2) void dkdv16_kernel(BwdParams p) {
+  using W = Dkv16Wave<T, D, CAUSAL, NW, BQ>;
+  using QT = typename W::QT;
+  constexpr int BK = NW * 16;
+  __shared__ __attribute__((aligned(1024))) char qa0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qa1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char da0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char da1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qt0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char qt1[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char dt0[QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char dt1[QT::BYTES];
+  __shared__ __attribute__((aligned(16))) float st0[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float st1[2 * BQ];
+
+  W w;
+  w.lane = threadIdx.x & 63;
+  // uniform across the wavefront: keeps the per-wavefront choices and LDS
+  // destinations below in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  w.g = w.lane >> 4;
+  int bh, kb;
+  map_block(p.BH, p.nblk, CAUSAL, false, bh, kb);
+  const int k_lo = kb * BK;
+  w.kw = k_lo + 16 * wave;
+  w.myk = w.kw + (w.lane & 15);
+  w.c = p.c;
+  w.shift = p.shift;
+
+  const View kv = head_view<D, STRIDED>(p, p.k, kK, bh), vv = head_view<D, STRIDED>(p, p.v, kV, bh);
+  const View qv = head_view<D, STRIDED>(p, p.q, kQ, bh), dov = head_view<D, STRIDED>(p, p.dout, kDO, bh);
+  const View dkv = head_view<D, STRIDED>(p, p.dk, kDK, bh), dvv = head_view<D, STRIDED>(p, p.dv, kDV, bh);
+  load_row_frags16<D>(w.kf, kv, w.myk, w.g);
+  load_row_frags16<D>(w.vf, vv, w.myk, w.g);
+#pragma unroll
+  for (int db = 0; db < W::DB; ++db) w.dk[db] = w.dv[db] = f32x4{};
+
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qv.base, qv.bytes);
+  const __amdgpu_buffer_rsrc_t rdo = rsrc(dov.base, dov.bytes);
+  const __amdgpu_buffer_rsrc_t rl = rsrc(p.lse + (size_t)bh * p.S, (uint32_t)p.S * 4);
+  const __amdgpu_buffer_rsrc_t rd = rsrc(p.delta + (size_t)bh * p.S, (uint32_t)p.S * 4);
+
+  // query tiles t0 .. n-1 (causal: only queries whose position i + shift
+  // reaches the block's first key)
+  const int t0 = CAUSAL ? max(0, k_lo - p.shift) / BQ : 0;
+  const int n = (p.S + BQ - 1) / BQ;
+  const uint32_t tq = (uint32_t)BQ * qv.rs, tdo = (uint32_t)BQ * dov.rs;  // bytes per query tile
+
+  float sv = 0.f;
+  if (t0 < n) {
+    QT::issue_a(rq, t0 * tq, qa0, wave, w.lane, qv.rs);
+    QT::issue_a(rdo, t0 * tdo, da0, wave, w.lane, dov.rs);
+    QT::issue_t(rq, t0 * tq, qt0, wave, w.lane, qv.rs);
+    QT::issue_t(rdo, t0 * tdo, dt0, wave, w.lane, dov.rs);
+    sv = load_stats16<BQ>(rl, rd, t0 * BQ, wave, w.lane);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  put_stats16<BQ>(st0, sv, wave, w.lane);
+  barrier();
+  for (int t = t0; t < n; t += 2) {
+    if (t + 1 < n) {
+      QT::issue_a(rq, (t + 1) * tq, qa1, wave, w.lane, qv.rs);
+      QT::issue_a(rdo, (t + 1) * tdo, da1, wave, w.lane, dov.rs);
+      QT::issue_t(rq, (t + 1) * tq, qt1, wave, w.lane, qv.rs);
+      QT::issue_t(rdo, (t + 1) * tdo, dt1, wave, w.lane, dov.rs);
+      sv = load_stats16<BQ>(rl, rd, (t + 1) * BQ, wave, w.lane);
+    }
+    if (w.active(t * BQ)) {
+      if (w.masked(t * BQ)) w.template step<true>(qa0, da0, qt0, dt0, st0, t * BQ);
+      else w.template step<false>(qa0, da0, qt0, dt0, st0, t * BQ);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (t + 1 >= n) break;
+    put_stats16<BQ>(st1, sv, wave, w.lane);
+    barrier();
+    if (t + 2 < n) {
+      QT::issue_a(rq, (t + 2) * tq, qa0, wave, w.lane, qv.rs);
+      QT::issue_a(rdo, (t + 2) * tdo, da0, wave, w.lane, dov.rs);
+      QT::issue_t(rq, (t + 2) * tq, qt0, wave, w.lane, qv.rs);
+      QT::issue_t(rdo, (t + 2) * tdo, dt0, wave, w.lane, dov.rs);
+      sv = load_stats16<BQ>(rl, rd, (t + 2) * BQ, wave, w.lane);
+    }
+    if (w.active((t + 1) * BQ)) {
+      if (w.masked((t + 1) * BQ)) w.template step<true>(qa1, da1, qt1, dt1, st1, (t + 1) * BQ);
+      else w.template step<false>(qa1, da1, qt1, dt1, st1, (t + 1) * BQ);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (t + 2 < n) put_stats16<BQ>(st0, sv, wave, w.lane);
+    barrier();
+  }
+  store_row16<T, D>(w.dk, p.scale, dkv, w.myk, w.g);
+  store_row16<T, D>(w.dv, 1.0f, dvv, w.myk, w.g);
+}
+
 // ------------------------------------------------------------------ launch
 
 // Wavefronts per dq_kernel work-group: eight (two per SIMD) up to d = 128;
@@ -615,6 +907,14 @@ template <int D>
 constexpr int dq_key_tile() { return D == 64 ? 64 : 32; }
 template <int D>
 constexpr int dkdv_query_tile() { return D == 64 ? 64 : 32; }
+// The 16-key dK/dV kernel (d = 128): eight wavefronts (128 keys, two
+// wavefronts per SIMD) and 32-query tiles.  Measured against four
+// wavefronts with two work-groups per CU (-9 %) and 64-query tiles (-16 %,
+// the causal variants spill).
+template <int D>
+constexpr int dkdv16_waves() { return 8; }
+template <int D>
+constexpr int dkdv16_query_tile() { return 32; }
 
 template <typename T, int D, bool CAUSAL, bool STRIDED>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
@@ -667,13 +967,23 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
 
-  constexpr int NW = dkdv_waves<D>();
-  constexpr int BK = NW * 32;
-  p.nblk = (a.Sk + BK - 1) / BK;
-  if (p.nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, NW, dkdv_query_tile<D>(), STRIDED>),
-                     dim3((unsigned)(p.nblk * p.BH)), dim3(NW * 64), 0, stream, p);
-  return hipGetLastError();
+  if constexpr (D == 128) {
+    constexpr int NW = dkdv16_waves<D>();
+    constexpr int BK = NW * 16;
+    p.nblk = (a.Sk + BK - 1) / BK;
+    if (p.nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, NW, dkdv16_query_tile<D>(), STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
+                       dim3(NW * 64), 0, stream, p);
+    return hipGetLastError();
+  } else {
+    constexpr int NW = dkdv_waves<D>();
+    constexpr int BK = NW * 32;
+    p.nblk = (a.Sk + BK - 1) / BK;
+    if (p.nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((dkdv_kernel<T, D, CAUSAL, NW, dkdv_query_tile<D>(), STRIDED>),
+                       dim3((unsigned)(p.nblk * p.BH)), dim3(NW * 64), 0, stream, p);
+    return hipGetLastError();
+  }
 }
 
 template <typename T, int D, bool STRIDED>
@@ -709,7 +1019,7 @@ long long bwd_grid_size(const BwdArgs& a) {
   const long long bh = (long long)a.B * a.H;
   const int bm = (a.d > 128 ? bwd::dq_waves<256>() : bwd::dq_waves<64>()) * 32;
   const long long dq = (long long)((a.S + bm - 1) / bm) * bh;
-  const int bk = (a.d == 64 ? bwd::dkdv_waves<64>() : bwd::dkdv_waves<128>()) * 32;
+  const int bk = a.d == 64 ? bwd::dkdv_waves<64>() * 32 : a.d == 128 ? bwd::dkdv16_waves<128>() * 16 : bwd::dkdv_waves<256>() * 32;
   const long long dkdv = (long long)((a.Sk + bk - 1) / bk) * bh;
   return dq > dkdv ? dq : dkdv;
 }
