@@ -635,6 +635,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
 //     operand with m = column 16 db + l%16 and k = rows 32 ch +
 //     {4 (l/16) .. +4, 16 + 4 (l/16) .. +4}: the order in which pack16 puts
 //     two C-layout tiles into one B operand.
+template <typename T>
+__device__ __forceinline__ f32x4 mma16(i16x8 a, i16x8 b, f32x4 c);
+
+template <>
+__device__ __forceinline__ f32x4 mma16<__bf16>(i16x8 a, i16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x4 mma16<_Float16>(i16x8 a, i16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
 template <int D, int NW, int ROWS>
 struct Tile16 {
   static constexpr int KS = D / 32;
@@ -722,8 +737,8 @@ struct Dkv16Wave {
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        s[qb] = Elem<T>::mma16(QT::frag_a(qA, qb, kk, lane), kf[kk], s[qb]);
-        dp[qb] = Elem<T>::mma16(QT::frag_a(dA, qb, kk, lane), vf[kk], dp[qb]);
+        s[qb] = mma16<T>(QT::frag_a(qA, qb, kk, lane), kf[kk], s[qb]);
+        dp[qb] = mma16<T>(QT::frag_a(dA, qb, kk, lane), vf[kk], dp[qb]);
       }
     i16x8 pf[NCH], dsf[NCH];
 #pragma unroll
@@ -754,8 +769,8 @@ struct Dkv16Wave {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
-        dv[db] = Elem<T>::mma16(QT::frag_t(dT, db, ch, lane), pf[ch], dv[db]);
-        dk[db] = Elem<T>::mma16(QT::frag_t(qT, db, ch, lane), dsf[ch], dk[db]);
+        dv[db] = mma16<T>(QT::frag_t(dT, db, ch, lane), pf[ch], dv[db]);
+        dk[db] = mma16<T>(QT::frag_t(qT, db, ch, lane), dsf[ch], dk[db]);
       }
   }
 };

@@ -40,10 +40,6 @@ struct Elem<__bf16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  static __device__ __forceinline__ f32x4 mma16(i16x8 a, i16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
   static __device__ __forceinline__ unsigned pack(float x, float y) {
     bf16x2 r = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(unsigned, r);
@@ -71,10 +67,6 @@ template <>
 struct Elem<_Float16> {
   static __device__ __forceinline__ f32x16 mma(i16x8 a, i16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 mma16(i16x8 a, i16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ unsigned pack(float x, float y) {
