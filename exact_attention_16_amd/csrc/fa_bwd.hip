@@ -31,7 +31,7 @@
 //   one key; LSE and D of the tile's queries come from LDS), then
 //   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
 //   At d = 128, dkdv16_kernel does the same with 16 keys per wavefront on
-//   16x16x32 MFMAs, so that two wavefronts share each SIMD.
+//   16x16x32 MFMAs, so that three wavefronts share each SIMD.
 // Tiles move HBM -> LDS with direct-to-LDS buffer loads in the same
 // fragment-major layouts as the forward kernel, double-buffered.
 
@@ -612,9 +612,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
 // At d = 128 the 32-key wavefront above holds 128 accumulator registers for
 // dK and dV alone and needs more than half of a SIMD's register file, so a
 // SIMD runs one wavefront and its exp / dS work never overlaps matrix work.
-// This variant gives each wavefront 16 keys on v_mfma_f32_16x16x32: half the
-// accumulators, two wavefronts per SIMD, for twice the LDS operand bytes per
-// FLOP.
+// dkdv16_kernel gives each wavefront 16 keys on v_mfma_f32_16x16x32: a
+// quarter of the accumulator registers per wavefront (146-164 VGPRs in all),
+// four wavefronts per work-group and three work-groups per CU, so each SIMD
+// interleaves three wavefronts whose barriers are independent.  The price is
+// twice the LDS operand bytes per FLOP.
 //
 // Lane layouts (checked on the MI355X with an in-bounds probe):
 //   v_mfma_f32_16x16x32: A (16 x 32) lane l holds row l%16, k = 8 (l/16) ..
@@ -624,17 +626,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
 //     u%4 of the 4-element reads of lanes 4 j + u/4, j = 0..3 (the group's
 //     reads as a 4 x 16 block, transposed).
 
-// Tiles of ROWS rows x D columns in two LDS layouts:
-//   A16 layout: 1 KiB block (rb, kk) holds, at lane l, row 16 rb + l%16,
-//     columns 32 kk + 8 (l/16) .. +8: the A operand of a 16x16x32 MFMA whose
-//     m index is the row and whose k index is the column;
-//   T16 layout: block (rb, dp) holds two 512-byte halves x, one per 16-column
-//     d-block 2 dp + x; in a half, the 8 bytes at lane L are row
-//     16 rb + 4 (L/16) + (L%16)/4, columns 16 (2 dp + x) + 4 (L%4) .. +4.
-//     Two transposing reads (rb = 2 ch, 2 ch + 1) then give lane l the A
-//     operand with m = column 16 db + l%16 and k = rows 32 ch +
-//     {4 (l/16) .. +4, 16 + 4 (l/16) .. +4}: the order in which pack16 puts
-//     two C-layout tiles into one B operand.
 template <typename T>
 __device__ __forceinline__ f32x4 mma16(i16x8 a, i16x8 b, f32x4 c);
 
@@ -650,6 +641,13 @@ __device__ __forceinline__ f32x4 mma16<_Float16>(i16x8 a, i16x8 b, f32x4 c) {
                                                 0);
 }
 
+// Q and dO tiles of ROWS rows x D columns, staged once in a swizzled layout
+// that serves both the plain 16-byte operand reads of S and dP and the
+// transposing reads of dV and dK.  Slot s (16 bytes) of 1 KiB block (rb, kk)
+// holds row 16 rb + ((s % 16) ^ 8 ((s / 16) % 2)), columns 32 kk + 8 (s / 16)
+// .. +8.  A transposing read fetches 4 consecutive columns of 4 rows per
+// 16-lane group; without the swizzle the column chunks 8 apart would share
+// banks, with it each 32-lane half covers all 64 banks once.
 template <int D, int NW, int ROWS>
 struct Tile16 {
   static constexpr int KS = D / 32;
@@ -657,43 +655,47 @@ struct Tile16 {
   static constexpr int LOADS = BYTES / (NW * 1024);
   static_assert(ROWS % 32 == 0 && LOADS * NW * 1024 == BYTES, "tile must split evenly over wavefronts");
 
-  static __device__ __forceinline__ void issue_a(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
-                                                 int lane, uint32_t rs) {
+  // each lane fetches the 16 bytes that belong at its slot
+  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
+                                               int lane, uint32_t rs) {
+    const int c = lane >> 4;
+    const int q = (lane & 15) ^ ((c & 1) << 3);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int f = i * NW + wave;  // block (rb, kk)
       const int rb = f / KS, kk = f % KS;
-      const uint32_t off = base + (uint32_t)(rb * 16 + (lane & 15)) * rs + (kk * 32 + (lane >> 4) * 8) * 2;
+      const uint32_t off = base + (uint32_t)(rb * 16 + q) * rs + (kk * 32 + c * 8) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + f * 1024), 16, off, 0, 0, 0);
     }
   }
 
-  // Each lane fetches the 16 bytes that belong at its 16-byte slot: the two
-  // 8-byte reads 2 (l%32), 2 (l%32) + 1 of half l/32.
-  static __device__ __forceinline__ void issue_t(__amdgpu_buffer_rsrc_t r, uint32_t base, char* dst, int wave,
-                                                 int lane, uint32_t rs) {
-    const int x = lane >> 5, lp = lane & 31;
-    const int row = 4 * (lp >> 3) + ((lp & 7) >> 1);
-    const int col = x * 16 + (lp & 1) * 8;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int f = i * NW + wave;  // block (rb, dp)
-      const int rb = f / KS, dp = f % KS;
-      const uint32_t off = base + (uint32_t)(rb * 16 + row) * rs + (dp * 32 + col) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + f * 1024), 16, off, 0, 0, 0);
-    }
+  // byte offset of lane l's A operand in a block: row l % 16, columns
+  // 8 (l / 16) .. +8
+  static __device__ __forceinline__ int a_off(int lane) {
+    const int c = lane >> 4;
+    return 16 * (16 * c + ((lane & 15) ^ ((c & 1) << 3)));
+  }
+  // byte offset of lane l = 16 g + u's transposing read in the first half of a
+  // block: row 4 g + u / 4, columns 4 (u % 4) .. +4 (the second half, +512,
+  // holds columns 16 .. 31)
+  static __device__ __forceinline__ int t_off(int lane) {
+    const int g = lane >> 4, u = lane & 15, a = u & 3, h = a >> 1;
+    return 256 * h + 16 * ((4 * g + (u >> 2)) ^ (8 * h)) + 8 * (a & 1);
   }
 
-  static __device__ __forceinline__ i16x8 frag_a(const char* t, int rb, int kk, int lane) {
-    return *(const i16x8*)(t + (rb * KS + kk) * 1024 + lane * 16);
+  static __device__ __forceinline__ i16x8 frag_a(const char* t, int rb, int kk, int aoff) {
+    return *(const i16x8*)(t + (rb * KS + kk) * 1024 + aoff);
   }
 
-  static __device__ __forceinline__ i16x8 frag_t(const char* t, int db, int ch, int lane) {
+  // A operand with m = columns 16 db .. +16 and k = rows 32 ch + {4 (l/16)
+  // .. +4, 16 + 4 (l/16) .. +4}: the order in which pack16 puts a pair of C
+  // tiles into one B operand
+  static __device__ __forceinline__ i16x8 frag_t(const char* t, int db, int ch, int toff) {
     i16x4 half[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int blk = (2 * ch + tt) * KS + (db >> 1);
-      half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + blk * 1024 + (db & 1) * 512 + lane * 8));
+      half[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + blk * 1024 + (db & 1) * 512 + toff));
     }
     return __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
   }
@@ -713,42 +715,44 @@ template <typename T, int D, bool CAUSAL, int NW, int BQ>
 struct Dkv16Wave {
   using QT = Tile16<D, NW, BQ>;
   static constexpr int KS = D / 32;
-  static constexpr int DB = D / 16;   // 16-column d-blocks of dK, dV
-  static constexpr int QB = BQ / 16;  // 16-query blocks of S, dP
-  static constexpr int NCH = BQ / 32; // 32-query chunks of the dV, dK products
+  static constexpr int DB = D / 16;    // 16-column d-blocks of dK, dV
+  static constexpr int QB = BQ / 16;   // 16-query blocks of S, dP
+  static constexpr int NCH = BQ / 32;  // 32-query chunks of the dV, dK products
 
-  int lane, g, kw, myk, shift;
+  int lane, g, kw, myk, shift, aoff, toff;
   float c;
   i16x8 kf[KS], vf[KS];
   f32x4 dk[DB], dv[DB];
+  f32x4 s[QB], dp[QB];
+  i16x8 pf[NCH], dsf[NCH];
 
   __device__ __forceinline__ bool active(int q0) const { return !(CAUSAL && q0 + BQ - 1 + shift < kw); }
   __device__ __forceinline__ bool masked(int q0) const { return CAUSAL && q0 + shift < kw + 15; }
 
-  // One query tile: qA, dA = Q, dO (A16 layout); qT, dT = Q, dO (T16
-  // layout); st = the tile's LSE in log2 units (floats 0..BQ-1), then D.
-  template <bool MASKED>
-  __device__ __forceinline__ void step(const char* qA, const char* dA, const char* qT, const char* dT,
-                                       const float* st, int q0) {
-    f32x4 s[QB], dp[QB];
+  // S = Q K^T and dP = dO V^T of a query tile (qA, dA: Q, dO)
+  __device__ __forceinline__ void scores(const char* qA, const char* dA) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = dp[qb] = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        s[qb] = mma16<T>(QT::frag_a(qA, qb, kk, lane), kf[kk], s[qb]);
-        dp[qb] = mma16<T>(QT::frag_a(dA, qb, kk, lane), vf[kk], dp[qb]);
+        s[qb] = mma16<T>(QT::frag_a(qA, qb, kk, aoff), kf[kk], s[qb]);
+        dp[qb] = mma16<T>(QT::frag_a(dA, qb, kk, aoff), vf[kk], dp[qb]);
       }
-    i16x8 pf[NCH], dsf[NCH];
+  }
+
+  // P and dS from the scores; st = the tile's LSE in log2 units (floats
+  // 0..BQ-1), then D
+  template <bool MASKED>
+  __device__ __forceinline__ void weights(const float* st, int q0) {
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       float pe[8], de[8];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int qb = 2 * ch + tt;
-        // queries 16 qb + 4 g + (0..3)
-        const int qi = qb * 16 + 4 * g;
+        const int qi = qb * 16 + 4 * g;  // queries 16 qb + 4 g + (0..3)
         const float4 l4 = *(const float4*)(st + qi);
         const float4 d4 = *(const float4*)(st + BQ + qi);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
@@ -765,13 +769,29 @@ struct Dkv16Wave {
       pf[ch] = pack16<T>(pe);
       dsf[ch] = pack16<T>(de);
     }
+  }
+
+  // dV^T += dO^T P and dK^T += Q^T dS
+  __device__ __forceinline__ void grads(const char* qA, const char* dA) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
-        dv[db] = mma16<T>(QT::frag_t(dT, db, ch, lane), pf[ch], dv[db]);
-        dk[db] = mma16<T>(QT::frag_t(qT, db, ch, lane), dsf[ch], dk[db]);
+        dv[db] = mma16<T>(QT::frag_t(dA, db, ch, toff), pf[ch], dv[db]);
+        dk[db] = mma16<T>(QT::frag_t(qA, db, ch, toff), dsf[ch], dk[db]);
       }
+  }
+
+  // One query tile.  The phases stay apart: letting the scheduler hoist one
+  // phase's LDS operand reads into another raises the register count past
+  // what three wavefronts per SIMD allow.
+  __device__ __forceinline__ void step(const char* qA, const char* dA, const float* st, int q0) {
+    scores(qA, dA);
+    __builtin_amdgcn_sched_barrier(0);
+    if (masked(q0)) weights<true>(st, q0);
+    else weights<false>(st, q0);
+    __builtin_amdgcn_sched_barrier(0);
+    grads(qA, dA);
   }
 };
 
@@ -801,9 +821,9 @@ __device__ __forceinline__ void store_row16(const f32x4 (&acc)[D / 16], float mu
   }
 }
 
-// LSE (times log2 e) and D of a query tile: wavefront 0 loads the LSE values,
-// wavefront 1 the D values, one per lane (rows past the sequence read 0);
-// put_stats16 writes them to LDS once the loads have landed.
+// LSE and D of a query tile: wavefront 0 loads the LSE values, wavefront 1
+// the D values, one per lane (rows past the sequence read 0); put_stats16
+// writes them to LDS, the LSE times log2 e, once the loads have landed.
 template <int BQ>
 __device__ __forceinline__ float load_stats16(__amdgpu_buffer_rsrc_t rl, __amdgpu_buffer_rsrc_t rd, int q0, int wave,
                                               int lane) {
@@ -818,7 +838,7 @@ __device__ __forceinline__ void put_stats16(float* st, float v, int wave, int la
 }
 
 template <typename T, int D, bool CAUSAL, int NW, int BQ, bool STRIDED>
-__global__ __launch_bounds__(NW * 64, 2) void dkdv16_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, 3) void dkdv16_kernel(BwdParams p) {
   using W = Dkv16Wave<T, D, CAUSAL, NW, BQ>;
   using QT = typename W::QT;
   constexpr int BK = NW * 16;
@@ -826,10 +846,6 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv16_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char qa1[QT::BYTES];
   __shared__ __attribute__((aligned(1024))) char da0[QT::BYTES];
   __shared__ __attribute__((aligned(1024))) char da1[QT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char qt0[QT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char qt1[QT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char dt0[QT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char dt1[QT::BYTES];
   __shared__ __attribute__((aligned(16))) float st0[2 * BQ];
   __shared__ __attribute__((aligned(16))) float st1[2 * BQ];
 
@@ -839,6 +855,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv16_kernel(BwdParams p) {
   // destinations below in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   w.g = w.lane >> 4;
+  w.aoff = QT::a_off(w.lane);
+  w.toff = QT::t_off(w.lane);
   int bh, kb;
   map_block(p.BH, p.nblk, CAUSAL, false, bh, kb);
   const int k_lo = kb * BK;
@@ -868,45 +886,30 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv16_kernel(BwdParams p) {
 
   float sv = 0.f;
   if (t0 < n) {
-    QT::issue_a(rq, t0 * tq, qa0, wave, w.lane, qv.rs);
-    QT::issue_a(rdo, t0 * tdo, da0, wave, w.lane, dov.rs);
-    QT::issue_t(rq, t0 * tq, qt0, wave, w.lane, qv.rs);
-    QT::issue_t(rdo, t0 * tdo, dt0, wave, w.lane, dov.rs);
+    QT::issue(rq, t0 * tq, qa0, wave, w.lane, qv.rs);
+    QT::issue(rdo, t0 * tdo, da0, wave, w.lane, dov.rs);
     sv = load_stats16<BQ>(rl, rd, t0 * BQ, wave, w.lane);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   put_stats16<BQ>(st0, sv, wave, w.lane);
   barrier();
-  for (int t = t0; t < n; t += 2) {
+  // tile t in (cq, cd, cs); tile t + 1 loaded into (nq, nd, ns)
+  auto step = [&](int t, const char* cq, const char* cd, const float* cs, char* nq, char* nd, float* ns) {
     if (t + 1 < n) {
-      QT::issue_a(rq, (t + 1) * tq, qa1, wave, w.lane, qv.rs);
-      QT::issue_a(rdo, (t + 1) * tdo, da1, wave, w.lane, dov.rs);
-      QT::issue_t(rq, (t + 1) * tq, qt1, wave, w.lane, qv.rs);
-      QT::issue_t(rdo, (t + 1) * tdo, dt1, wave, w.lane, dov.rs);
+      QT::issue(rq, (t + 1) * tq, nq, wave, w.lane, qv.rs);
+      QT::issue(rdo, (t + 1) * tdo, nd, wave, w.lane, dov.rs);
       sv = load_stats16<BQ>(rl, rd, (t + 1) * BQ, wave, w.lane);
     }
-    if (w.active(t * BQ)) {
-      if (w.masked(t * BQ)) w.template step<true>(qa0, da0, qt0, dt0, st0, t * BQ);
-      else w.template step<false>(qa0, da0, qt0, dt0, st0, t * BQ);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (w.active(t * BQ)) w.step(cq, cd, cs, t * BQ);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (t + 1 < n) put_stats16<BQ>(ns, sv, wave, w.lane);
+    barrier();
+  };
+  for (int t = t0; t < n; t += 2) {
+    step(t, qa0, da0, st0, qa1, da1, st1);
     if (t + 1 >= n) break;
-    put_stats16<BQ>(st1, sv, wave, w.lane);
-    barrier();
-    if (t + 2 < n) {
-      QT::issue_a(rq, (t + 2) * tq, qa0, wave, w.lane, qv.rs);
-      QT::issue_a(rdo, (t + 2) * tdo, da0, wave, w.lane, dov.rs);
-      QT::issue_t(rq, (t + 2) * tq, qt0, wave, w.lane, qv.rs);
-      QT::issue_t(rdo, (t + 2) * tdo, dt0, wave, w.lane, dov.rs);
-      sv = load_stats16<BQ>(rl, rd, (t + 2) * BQ, wave, w.lane);
-    }
-    if (w.active((t + 1) * BQ)) {
-      if (w.masked((t + 1) * BQ)) w.template step<true>(qa1, da1, qt1, dt1, st1, (t + 1) * BQ);
-      else w.template step<false>(qa1, da1, qt1, dt1, st1, (t + 1) * BQ);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    if (t + 2 < n) put_stats16<BQ>(st0, sv, wave, w.lane);
-    barrier();
+    step(t + 1, qa1, da1, st1, qa0, da0, st0);
   }
   store_row16<T, D>(w.dk, p.scale, dkv, w.myk, w.g);
   store_row16<T, D>(w.dv, 1.0f, dvv, w.myk, w.g);
@@ -922,12 +925,10 @@ template <int D>
 constexpr int dq_key_tile() { return D == 64 ? 64 : 32; }
 template <int D>
 constexpr int dkdv_query_tile() { return D == 64 ? 64 : 32; }
-// The 16-key dK/dV kernel (d = 128): eight wavefronts (128 keys, two
-// wavefronts per SIMD) and 32-query tiles.  Measured against four
-// wavefronts with two work-groups per CU (-9 %) and 64-query tiles (-16 %,
-// the causal variants spill).
+// The 16-key dK/dV kernel (d = 128): four wavefronts (64 keys) per
+// work-group, three work-groups per CU, 32-query tiles.
 template <int D>
-constexpr int dkdv16_waves() { return 8; }
+constexpr int dkdv16_waves() { return 4; }
 template <int D>
 constexpr int dkdv16_query_tile() { return 32; }
 
@@ -983,11 +984,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   }
 
   if constexpr (D == 128) {
+    // Non-causal problems run the causal code with shift = Sk (every key
+    // kept): the non-causal instantiation needs more registers than three
+    // wavefronts per SIMD allow (40-64 B of spill).
     constexpr int NW = dkdv16_waves<D>();
     constexpr int BK = NW * 16;
     p.nblk = (a.Sk + BK - 1) / BK;
     if (p.nblk == 0) return hipSuccess;
-    hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, NW, dkdv16_query_tile<D>(), STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
+    hipLaunchKernelGGL((dkdv16_kernel<T, D, true, NW, dkdv16_query_tile<D>(), STRIDED>), dim3((unsigned)(p.nblk * p.BH)),
                        dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
   } else {
