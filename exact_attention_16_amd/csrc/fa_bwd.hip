@@ -32,8 +32,9 @@
 //   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
 //   At d = 128, dkdv16_kernel does the same with 16 keys per wavefront on
 //   16x16x32 MFMAs, so that three wavefronts share each SIMD.
-// Tiles move HBM -> LDS with direct-to-LDS buffer loads in the same
-// fragment-major layouts as the forward kernel, double-buffered.
+// Tiles move HBM -> LDS with direct-to-LDS buffer loads, double-buffered:
+// in the forward kernel's fragment-major layouts, or for dkdv16_kernel in one
+// swizzled layout per tile (Tile16).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -612,9 +613,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
 // At d = 128 the 32-key wavefront above holds 128 accumulator registers for
 // dK and dV alone and needs more than half of a SIMD's register file, so a
 // SIMD runs one wavefront and its exp / dS work never overlaps matrix work.
-// dkdv16_kernel gives each wavefront 16 keys on v_mfma_f32_16x16x32: a
-// quarter of the accumulator registers per wavefront (146-164 VGPRs in all),
-// four wavefronts per work-group and three work-groups per CU, so each SIMD
+// dkdv16_kernel gives each wavefront 16 keys on v_mfma_f32_16x16x32: half
+// the accumulator registers (154-158 VGPRs in all, no AGPRs), four
+// wavefronts per work-group and three work-groups per CU, so each SIMD
 // interleaves three wavefronts whose barriers are independent.  The price is
 // twice the LDS operand bytes per FLOP.
 //
