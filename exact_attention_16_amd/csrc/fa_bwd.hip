@@ -30,8 +30,8 @@
 //   wavefront walks the query tiles: S = Q K^T and dP = dO V^T (each lane holds
 //   one key; LSE and D of the tile's queries come from LDS), then
 //   dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
-//   At d = 128, dkdv16_kernel does the same with 16 keys per wavefront on
-//   16x16x32 MFMAs, so that three wavefronts share each SIMD.
+//   At d >= 128, dkdv16_kernel does the same with 16 keys per wavefront on
+//   16x16x32 MFMAs, so that two or three wavefronts share each SIMD.
 // Tiles move HBM -> LDS with direct-to-LDS buffer loads, double-buffered:
 // in the forward kernel's fragment-major layouts, or for dkdv16_kernel in one
 // swizzled layout per tile (Tile16).
@@ -617,7 +617,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 1 : 2) void dkdv_kernel(BwdParam
 // the accumulator registers (154-158 VGPRs in all, no AGPRs), four
 // wavefronts per work-group and three work-groups per CU, so each SIMD
 // interleaves three wavefronts whose barriers are independent.  The price is
-// twice the LDS operand bytes per FLOP.
+// twice the LDS operand bytes per FLOP.  The wide heads (d = 192, 256) run
+// it too, at two wavefronts per SIMD (202-256 VGPRs) where the 32-key
+// kernel fits only one.
 //
 // Lane layouts (checked on the MI355X with an in-bounds probe):
 //   v_mfma_f32_16x16x32: A (16 x 32) lane l holds row l%16, k = 8 (l/16) ..
@@ -843,7 +845,7 @@ __device__ __forceinline__ void put_stats16(float* st, float v, int wave, int la
 }
 
 template <typename T, int D, bool CAUSAL, int NW, int BQ, bool STRIDED>
-__global__ __launch_bounds__(NW * 64, 3) void dkdv16_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, D == 128 ? 3 : 2) void dkdv16_kernel(BwdParams p) {
   using W = Dkv16Wave<T, D, CAUSAL, NW, BQ>;
   using QT = typename W::QT;
   constexpr int BK = NW * 16;
@@ -930,8 +932,9 @@ template <int D>
 constexpr int dq_key_tile() { return D == 64 ? 64 : 32; }
 template <int D>
 constexpr int dkdv_query_tile() { return D == 64 ? 64 : 32; }
-// The 16-key dK/dV kernel (d = 128): four wavefronts (64 keys) per
-// work-group, three work-groups per CU, 32-query tiles.
+// The 16-key dK/dV kernel (d >= 128): four wavefronts (64 keys) per
+// work-group, 32-query tiles; three work-groups per CU at d = 128, two at
+// d = 192 and 256.
 template <int D>
 constexpr int dkdv16_waves() { return 4; }
 template <int D>
@@ -988,10 +991,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
 
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     // Non-causal problems run the causal code with shift = Sk (every key
-    // kept): the non-causal instantiation needs more registers than three
-    // wavefronts per SIMD allow (40-64 B of spill).
+    // kept): at d = 128 the non-causal instantiation needs more registers
+    // than three wavefronts per SIMD allow (40-64 B of spill).
     constexpr int NW = dkdv16_waves<D>();
     constexpr int BK = NW * 16;
     p.nblk = (a.Sk + BK - 1) / BK;
@@ -1043,7 +1046,7 @@ long long bwd_grid_size(const BwdArgs& a) {
   const long long bh = (long long)a.B * a.H;
   const int bm = (a.d > 128 ? bwd::dq_waves<256>() : bwd::dq_waves<64>()) * 32;
   const long long dq = (long long)((a.S + bm - 1) / bm) * bh;
-  const int bk = a.d == 64 ? bwd::dkdv_waves<64>() * 32 : a.d == 128 ? bwd::dkdv16_waves<128>() * 16 : bwd::dkdv_waves<256>() * 32;
+  const int bk = a.d == 64 ? bwd::dkdv_waves<64>() * 32 : bwd::dkdv16_waves<128>() * 16;
   const long long dkdv = (long long)((a.Sk + bk - 1) / bk) * bh;
   return dq > dkdv ? dq : dkdv;
 }
