@@ -153,10 +153,20 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       barrier();
     }
-    // (every LDS read of this block happened before the last barrier, so the
-    // next block's first K tile may overwrite the buffers)
-    w.store(p.o, p.lse, head_elems, bh);
+    // Every LDS read of this block happened before the last barrier, so the
+    // output tiles are staged in the K/V buffers (two wavefronts' 32-row
+    // tiles per buffer); the barrier after the store frees them for the next
+    // block's first K tile.  (The fast-softmax d = 64 variants, which run
+    // only long rows where the store is a small share, keep the direct store:
+    // staging cost them registers, 28 -> 44 B of spill, and 1-3 %.)
+    if constexpr (D == 64 && FAST) {
+      w.store(p.o, p.lse, head_elems, bh);
+    } else {
+      char* const buf = w.wave < 2 ? k_lds0 : w.wave < 4 ? k_lds1 : w.wave < 6 ? v_lds0 : v_lds1;
+      w.store_staged(p.o, p.lse, head_elems, bh, buf + (w.wave & 1) * 32 * W::ROW_BYTES);
+    }
     more = (kPersist && p.persist) ? cur.next(p, bh, qb) : false;
+    if (more) barrier();
   }
 }
 

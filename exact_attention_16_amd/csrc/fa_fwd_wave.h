@@ -565,6 +565,55 @@ struct FwdWave {
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rl, (uint32_t)myq * 4, 0, 0);
     }
   }
+
+  // store() with the output tile staged through LDS.  Storing straight from
+  // the accumulators, each instruction scatters 8-byte pieces over 32 rows,
+  // and a wavefront took about 4000 cycles to issue its O tile.  Here the
+  // lanes first write their pieces into `stage` (this wavefront's 32 x D
+  // tile of LDS, free once the block's last barrier is passed), then the
+  // wavefront stores whole rows, 16 contiguous bytes per lane.  The layout
+  // keeps both LDS accesses free of bank conflicts: 16-byte chunk c of row r
+  // sits at chunk c ^ f(r), and rows 16..31 swap the two 8-byte halves of
+  // each chunk (rows r and r + 16 share f(r)).
+  __device__ __forceinline__ void store_staged(void* o, float* lse, size_t head_elems, int bh, char* stage) const {
+    const float ltot = sum_with_partner(lsum);
+    const bool none = !(ltot > 0.f);
+    const float inv = none ? 0.f : 1.0f / out_divisor();
+    // f(r): rows of a multiple of 256 bytes start on the same bank, so
+    // spread rows 0..15 over the 16 chunks; rows of 128 or 384 bytes
+    // alternate between the two bank halves, so spread pairs of rows
+    constexpr bool kRowAligned = (ROW_BYTES / 4) % 64 == 0;
+    auto fr = [](int r) { return kRowAligned ? (r & 15) : ((r >> 1) & 7); };
+    {
+      const int r = col;
+      const int f = fr(r), gsw = (r >> 4) & 1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          u32x2 w;
+          w[0] = Elem<T>::pack(oacc[db][4 * rg + 0] * inv, oacc[db][4 * rg + 1] * inv);
+          w[1] = Elem<T>::pack(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv);
+          const int c = db * 4 + rg;  // columns 32 db + 8 rg .. +8
+          *(u32x2*)(stage + r * ROW_BYTES + ((c ^ f) * 16) + 8 * (h ^ gsw)) = w;
+        }
+    }
+    const __amdgpu_buffer_rsrc_t ro =
+        STRIDED ? rsrc(oh, o_bytes) : rsrc((const char*)o + head_elems * 2, head_bytes);
+#pragma unroll
+    for (int i = 0; i < 32 * ROW_BYTES / 1024; ++i) {
+      const int off = i * 1024 + lane * 16;
+      const int r = off / ROW_BYTES, c = (off % ROW_BYTES) / 16;
+      u32x4 v = *(const u32x4*)(stage + r * ROW_BYTES + ((c ^ fr(r)) * 16));
+      if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, o_row(qw + r) + c * 16, 0, 0);
+    }
+    if (h == 0) {
+      const __amdgpu_buffer_rsrc_t rl = rsrc(lse + (size_t)bh * S, (uint32_t)S * 4);
+      const float v = none ? -__builtin_inff() : (mc + __builtin_amdgcn_logf(ltot)) * 0.69314718055994531f;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rl, (uint32_t)myq * 4, 0, 0);
+    }
+  }
 };
 
 }  // namespace detail

@@ -107,7 +107,9 @@ __global__ __launch_bounds__(kWideWaves * 64, wide_waves_per_simd<D>()) void fwd
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     barrier();
   }
-  w.store(p.o, p.lse, head_elems, bh);
+  // the output tiles staged in the K buffers (two wavefronts' 32-row tiles
+  // per buffer; every LDS read happened before the last barrier)
+  w.store_staged(p.o, p.lse, head_elems, bh, (w.wave < 2 ? k_lds0 : k_lds1) + (w.wave & 1) * 32 * W::ROW_BYTES);
 }
 
 template <typename T, int D, bool CAUSAL, bool TAIL, bool STRIDED>
