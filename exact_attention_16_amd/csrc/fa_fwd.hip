@@ -68,7 +68,9 @@ namespace detail {
 // issues its share of K_{k+1} and V_k into the buffers that the barrier after
 // step 2k-1 has freed; they must land by step 2k+2, which the vmcnt(0) wait
 // before the barrier ending step 2k+1 guarantees.  K_k lives in K buffer k%2
-// and V_k in V buffer k%2.
+// and V_k in V buffer k%2.  Steps 2n and 2n+1 issue no load and read no K
+// tile; they run after the step loop, where a persistent work-group loads
+// its next block's Q rows.
 // Occupancy: head dimension 128 runs one work-group per compute unit (two
 // wavefronts per SIMD, at most 256 VGPRs each); head dimension 64 fits two
 // (at most 128 VGPRs each), so one work-group's prologue, barriers and
@@ -77,6 +79,12 @@ namespace detail {
 // 128 VGPRs.)
 template <int D, bool CAUSAL, bool TAIL>
 constexpr int waves_per_simd() { return D == 64 ? 4 : 2; }
+
+// Variants launched as a persistent grid (see launch_t): d = 128 except the
+// ragged non-causal one, which spilled 100-220 B with the block loop.  At
+// d = 64 the loop cost registers, spills and 15-18 % at S >= 4096.
+template <int D, bool CAUSAL, bool TAIL>
+constexpr bool persistent_variant() { return D == 128 && (CAUSAL || !TAIL); }
 
 // FAST: unmasked tiles take the softmax without the row max when the weights'
 // range allows (FwdWave::softmax_impl).
@@ -102,9 +110,7 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
 
   // One query block per work-group, or (persistent grid) the work-group's
   // list of blocks one after the other.
-  // (only causal instantiations at d = 128 are launched persistent; the
-  // others keep the one-block code)
-  constexpr bool kPersist = CAUSAL && D == 128;
+  constexpr bool kPersist = persistent_variant<D, CAUSAL, TAIL>();
   BlockCursor<CAUSAL> cur;
   int bh, qb;
   bool more;
@@ -115,6 +121,12 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
     map_query_block<CAUSAL>(blockIdx.x, p.BH, p.nqb, bh, qb);
     more = true;
   }
+  // Persistent: the block after this one.  Its Q rows are fetched during
+  // this block's last two steps and its output store (once the block's last
+  // K Q^T has run, Q is not read again), so the next block's prologue loads
+  // only its first key tile.
+  int next_bh = 0, next_qb = 0;
+  bool prefetched = false;
   while (more) {
     const int q_lo = qb * W::BM;
     // Row blocks alternate between the groups (group 0: blocks 0, 2, 4, 6;
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
     // other.
     w.qw = q_lo + 32 * (2 * (w.wave & 3) + group);
     w.myq = w.qw + w.col;
-    const size_t head_elems = w.setup(p, bh);
+    const size_t head_elems = w.setup(p, bh, kPersist && prefetched);
 
     // keys this work-group visits (causal: up to its last row's position)
     const int kv_end = CAUSAL ? min(p.Sk, q_lo + W::BM + p.shift) : p.Sk;
@@ -133,24 +145,41 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
     w.issue_k(0, k_lds0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     barrier();
+    const bool has_next = (kPersist && p.persist) ? cur.next(p, next_bh, next_qb) : false;
+    const int next_qw = next_qb * W::BM + 32 * (2 * (w.wave & 3) + group);
 
-    for (int k = 0; k <= n; k += 2) {
+    // Steps 0 .. 2n-1; then steps 2n and 2n+1 (P V of the last tile and the
+    // softmax before it), which read neither Q nor a K buffer.
+    for (int k = 0; k < n; k += 2) {
       // ---- even k: K_k in buffer 0, V_{k-1} in buffer 1
       if (k + 1 < n) w.issue_k(k + 1, k_lds1);
-      if (k < n) w.issue_v(k, v_lds0);
+      w.issue_v(k, v_lds0);
       if (group == 0) w.mfma_phase(k, k_lds0, v_lds1); else w.soft_phase(k - 1);
       barrier();
       if (group == 0) w.soft_phase(k); else w.mfma_phase(k, k_lds0, v_lds1);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       barrier();
-      if (k + 1 > n) break;
+      if (k + 1 >= n) break;
       // ---- odd k+1: K_{k+1} in buffer 1, V_k in buffer 0
       if (k + 2 < n) w.issue_k(k + 2, k_lds0);
-      if (k + 1 < n) w.issue_v(k + 1, v_lds1);
+      w.issue_v(k + 1, v_lds1);
       if (group == 0) w.mfma_phase(k + 1, k_lds1, v_lds0); else w.soft_phase(k);
       barrier();
       if (group == 0) w.soft_phase(k + 1); else w.mfma_phase(k + 1, k_lds1, v_lds0);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      barrier();
+    }
+    // The next block's Q rows stay in flight through the last two steps and
+    // the output store.  (Issued after the loop, so that no read of Q inside
+    // it waits for them.  A load of the next key tile here would make the
+    // compiler wait for it before the LDS accesses below, whose buffer it
+    // cannot tell apart from K buffer 0.)
+    if (kPersist && has_next) w.prefetch_q(p, next_bh, next_qw);
+    {
+      const char* const vl = (n & 1) ? v_lds0 : v_lds1;  // V_{n-1}: buffer (n-1) % 2
+      if (group == 0) w.pv_phase(n, vl); else w.soft_phase(n - 1);
+      barrier();
+      if (group == 1) w.pv_phase(n, vl);
       barrier();
     }
     // Every LDS read of this block happened before the last barrier, so the
@@ -165,7 +194,10 @@ __global__ __launch_bounds__(NW * 64, (waves_per_simd<D, CAUSAL, TAIL>())) void 
       char* const buf = w.wave < 2 ? k_lds0 : w.wave < 4 ? k_lds1 : w.wave < 6 ? v_lds0 : v_lds1;
       w.store_staged(p.o, p.lse, head_elems, bh, buf + (w.wave & 1) * 32 * W::ROW_BYTES);
     }
-    more = (kPersist && p.persist) ? cur.next(p, bh, qb) : false;
+    more = has_next;
+    prefetched = has_next;
+    bh = next_bh;
+    qb = next_qb;
     if (more) barrier();
   }
 }
@@ -216,16 +248,17 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     p.osb = st[9]; p.osh = st[10]; p.o_rs = (uint32_t)(st[11] * 2);
   }
   long long grid = (long long)p.nqb * p.BH;
-  // Causal problems at d = 128 run a persistent grid: one work-group per
-  // compute unit, each working through its list of (long, short) query-block
-  // pairs, so every work-group gets the same number of key tiles (see
-  // BlockCursor).  (At d = 64 the loop cost registers, spills and 15-18 %
-  // at S >= 4096 on the MI355X, so d = 64 keeps one block per work-group.)
+  // The persistent variants run one work-group per compute unit, each
+  // working through its list of query blocks (causal: (long, short) pairs,
+  // so every work-group gets the same number of key tiles; see BlockCursor)
+  // and loading each block's Q rows during the previous block's last steps.
+  // Measured on the MI355X against one block per work-group: S = 512
+  // non-causal +9 %, S = 2048 causal +3 %, S = 8192 causal +2 %.
   p.persist = 0;
-  if (D == 128 && a.causal) {
+  if constexpr (persistent_variant<D, CAUSAL, TAIL>()) {
     // resident work-groups: (waves per SIMD x 4 SIMDs) / kWaves per compute unit
     const long long slots = (long long)device_cus(stream) * (waves_per_simd<D, CAUSAL, TAIL>() * 4 / kWaves);
-    const long long units = (long long)p.BH * ((p.nqb + 1) / 2);
+    const long long units = (long long)p.BH * (CAUSAL ? (p.nqb + 1) / 2 : p.nqb);
     if (slots > 0 && units > slots) {
       p.persist = 1;
       grid = slots;

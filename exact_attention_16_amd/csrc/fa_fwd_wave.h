@@ -155,8 +155,9 @@ struct FwdWave {
 
   // Lengths, scale, the head's Q/K/V/O bases and ranges from the launch
   // parameters, then this lane's Q row (qw, myq and the lane fields must be
-  // set).  Returns the dense head offset in elements (bh * S * D).
-  __device__ __forceinline__ size_t setup(const Params& p, int bh) {
+  // set), unless `q_loaded` (prefetch() has already issued it).  Returns the
+  // dense head offset in elements (bh * S * D).
+  __device__ __forceinline__ size_t setup(const Params& p, int bh, bool q_loaded = false) {
     S = p.S;
     Sk = p.Sk;
     shift = p.shift;
@@ -177,16 +178,31 @@ struct FwdWave {
       kh = (const char*)p.k + (b * p.ksb + hh * p.ksh) * 2;
       vh = (const char*)p.v + (b * p.vsb + hh * p.vsh) * 2;
       oh = (const char*)p.o + (b * p.osb + hh * p.osh) * 2;
-      load_q((const char*)p.q + (b * p.qsb + hh * p.qsh) * 2);
+      if (q_loaded) reset_rows(); else load_q((const char*)p.q + (b * p.qsb + hh * p.qsh) * 2);
     } else {
       const size_t kv_head_elems = (size_t)bh * p.Sk * D;
       head_bytes = (uint32_t)p.S * ROW_BYTES;
       kv_head_bytes = (uint32_t)p.Sk * ROW_BYTES;
       kh = (const char*)p.k + kv_head_elems * 2;
       vh = (const char*)p.v + kv_head_elems * 2;
-      load_q((const char*)p.q + head_elems * 2);
+      if (q_loaded) reset_rows(); else load_q((const char*)p.q + head_elems * 2);
     }
     return head_elems;
+  }
+
+  // The Q rows of the work-group's next query block (head nbh, first row nqw
+  // of this wavefront) into qf, issued while this block finishes (it reads
+  // qf no more once its last K Q^T has run).  setup(p, nbh, true) completes
+  // the switch (head strides and range sizes are the same for every head).
+  __device__ __forceinline__ void prefetch_q(const Params& p, int nbh, int nqw) {
+    const char* qh;
+    if constexpr (STRIDED) {
+      const int b = nbh / p.H, hh = nbh - b * p.H;
+      qh = (const char*)p.q + (b * p.qsb + hh * p.qsh) * 2;
+    } else {
+      qh = (const char*)p.q + (size_t)nbh * p.S * D * 2;
+    }
+    load_qf(qh, nqw + col);
   }
 
   // Does this wavefront have any unmasked key in the tile starting at k0?
@@ -194,12 +210,19 @@ struct FwdWave {
 
   // Q rows -> VGPRs as the B operand of S^T = K Q^T (rows >= S read as 0).
   __device__ __forceinline__ void load_q(const char* qh) {
+    load_qf(qh, myq);
+    reset_rows();
+  }
+  __device__ __forceinline__ void load_qf(const char* qh, int row) {
     const __amdgpu_buffer_rsrc_t rq = rsrc(qh, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      const uint32_t off = q_row(myq) + (kk * 16 + h * 8) * 2;
+      const uint32_t off = q_row(row) + (kk * 16 + h * 8) * 2;
       qf[kk] = __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
+  }
+  // A new block's running statistics and output accumulator.
+  __device__ __forceinline__ void reset_rows() {
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     m_used = -__builtin_inff();
@@ -526,6 +549,13 @@ struct FwdWave {
       if (do_pv) pv(vp);
       if (do_qk) scores(kc);
     }
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  // Phase MFMA(n) alone: P V of the last tile (no K Q^T).
+  __device__ __forceinline__ void pv_phase(int k, const char* vp) {
+    __builtin_amdgcn_s_setprio(1);
+    if (k >= 1 && active((k - 1) * BN)) pv(vp);
     __builtin_amdgcn_s_setprio(0);
   }
 
