@@ -373,7 +373,7 @@ def main():
     roof["algorithmic_bytes"] = algorithmic_bytes(w)
     roof["flops"] = f
     roof["mfma_frac"] = value / PEAK_MFMA_TFLOPS
-    in_order = w.d > 128 or (w.causal and w.S <= (2048 if w.d == 64 else 1024))
+    in_order = w.d > 128 or (w.causal and w.S <= (2048 if w.d == 64 else 512))
     roof["kernel"] = "fa::detail::fwd_wide_kernel" if in_order else "fa::detail::fwd_kernel"
     roof["launch_ms"] = ms
     roof["launch_stats"] = r["launch_stats"]

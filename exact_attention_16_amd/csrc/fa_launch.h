@@ -40,10 +40,13 @@ hipError_t launch_fwd_wide(const FwdArgs& a, hipStream_t stream);
 
 // Short causal problems run faster on the in-order kernel's 128-row blocks:
 // with few key tiles per block, finer blocks balance the triangular work
-// better than the ping-pong kernel's 256 rows (measured on the MI355X).
+// better than the ping-pong kernel's 256 rows (measured on the MI355X).  At
+// d = 128 the persistent ping-pong grid pairs long and short blocks, which
+// moves the crossover down: S = 1024 causal runs 8 % faster there, S = 512
+// ties.
 inline bool uses_in_order_kernel(const FwdArgs& a) {
   if (a.d > 128) return true;
-  return a.causal && a.Sk <= (a.d == 64 ? 2048 : 1024);
+  return a.causal && a.Sk <= (a.d == 64 ? 2048 : 512);
 }
 
 }  // namespace fa
