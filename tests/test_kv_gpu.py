@@ -96,6 +96,10 @@ def test_kv_scale_zero_rows_without_keys():
     (2, 16, 2048, 8192, 128, True),   # a prompt chunk after a cached 6k prefix
     (4, 32, 512, 16384, 64, False),
     (1, 8, 8192, 1024, 128, True),    # more queries than keys: 7168 rows per head see none
+    # more query blocks than compute units: the persistent grid, each block's
+    # Q rows loaded during the previous block
+    (2, 32, 4096, 6144, 128, False),
+    (2, 32, 4096, 6144, 128, True),
 ])
 def test_kv_large_sampled(B, H, Sq, Sk, d, causal):
     q, k, v = make_inputs_kv(B, H, Sq, Sk, d, "bf16", seed=70_800 + Sq + Sk)

@@ -111,12 +111,15 @@ def test_output_view_leaves_the_rest_untouched():
     assert (buf[mask] == 1234.0).all().item()
 
 
-def test_large_bshd_bitwise():
-    """The long causal workload's shape in BSHD storage: bitwise the dense result."""
-    q, k, v = (x.cuda() for x in make_inputs_kv(2, 16, 8192, 8192, 128, "bf16", seed=93_000))
-    say("strided large bshd")
-    o_dense, l_dense = fa.forward(q, k, v, causal=True)
-    o, lse = fa.forward(bshd(q), bshd(k), bshd(v), causal=True)
+@pytest.mark.parametrize("S,causal", [(8192, True), (4096, False)])
+def test_large_bshd_bitwise(S, causal):
+    """Shapes with more query blocks than compute units (the long causal
+    workload's, and a non-causal one; both run the persistent grid) in BSHD
+    storage: bitwise the dense result."""
+    q, k, v = (x.cuda() for x in make_inputs_kv(2, 16, S, S, 128, "bf16", seed=93_000 + S))
+    say(f"strided large bshd S={S} causal={causal}")
+    o_dense, l_dense = fa.forward(q, k, v, causal=causal)
+    o, lse = fa.forward(bshd(q), bshd(k), bshd(v), causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o, o_dense) and torch.equal(lse, l_dense)
 
