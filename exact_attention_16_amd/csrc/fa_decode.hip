@@ -282,6 +282,197 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (lane == 0) p.lse[row] = none ? -__builtin_inff() : m + __builtin_amdgcn_logf(sum) * 0.69314718055994531f;
 }
 
+// ------------------------------------------------ one query row (S_q = 1)
+//
+// With a single query row the scores are a matrix-vector product, so the
+// key and value rows go straight from HBM into registers (no LDS stage, no
+// MFMA), with the split plan, partial layout and merge of the kernel above.
+// Work-group = 4 wavefronts on one (head, key split).  One wavefront
+// instruction loads 1 KiB of whole rows: lane l holds 16-byte chunk l % LPR
+// of row l / LPR (LPR = lanes per row), U instructions each of K and V in
+// flight.  A row's score is the sum of its lanes' v_dot2 partial products
+// (DPP exchanges within the row's lanes).  Each lane keeps an online softmax
+// over the rows it sees: a reference max that trails the running max by at
+// most kDec1Margin binary orders (moved, with a rescale, only when a score
+// passes it), its row sum and the 8 output columns of its chunk.  The
+// 4 * (64 / LPR) streams of the work-group are merged through LDS at the end
+// into the split's partial row and LSE.
+
+constexpr float kDec1Margin = 8.0f;
+// Cache policy of the row loads: non-temporal (each K / V byte is read once).
+// Measured on the MI355X (1 GiB caches): 6.7 TB/s against 5.9 TB/s with the
+// default policy.
+constexpr int kDecode1LoadAux = 2;
+
+template <typename T>
+struct Dec1Elem;
+template <>
+struct Dec1Elem<__bf16> {
+  static __device__ __forceinline__ float dot2(unsigned a, unsigned b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+  }
+  static __device__ __forceinline__ float lo(unsigned x) { return __builtin_bit_cast(float, x << 16); }
+  static __device__ __forceinline__ float hi(unsigned x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
+};
+template <>
+struct Dec1Elem<_Float16> {
+  static __device__ __forceinline__ float dot2(unsigned a, unsigned b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+  }
+  static __device__ __forceinline__ float lo(unsigned x) { return (float)__builtin_bit_cast(f16x2, x)[0]; }
+  static __device__ __forceinline__ float hi(unsigned x) { return (float)__builtin_bit_cast(f16x2, x)[1]; }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Sum over each aligned group of LPR (8 or 16) lanes, in every lane of it:
+// swaps within pairs and quads, then the half-row and row mirrors.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror: lane i <-> 7 - i of each 8
+  if constexpr (LPR == 16) x += dpp_f32<0x140>(x);  // row_mirror: lane i <-> 15 - i of each 16
+  return x;
+}
+
+template <typename T, int D, int U, bool STRIDED>
+__global__ __launch_bounds__(256) void decode1_kernel(DecParams p) {
+  constexpr int ROW = D * 2;         // bytes per key / value row
+  constexpr int LPR = ROW / 16;      // lanes per row
+  constexpr int RPI = 64 / LPR;      // rows per wavefront instruction
+  constexpr int ITER = 4 * U * RPI;  // rows per work-group iteration
+  constexpr int STREAMS = 4 * RPI;
+  static_assert(LPR == 8 || LPR == 16, "d = 64 or 128");
+  static_assert((decode_tile_keys(D) * 1) % ITER == 0, "a split is a whole number of iterations");
+  using E = Dec1Elem<T>;
+  __shared__ float s_m[STREAMS], s_l[STREAMS];
+  __shared__ __attribute__((aligned(16))) float s_o[STREAMS * D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int chunk = lane % LPR, sub = lane / LPR;
+  const int split = blockIdx.x % p.nsplit;
+  const int bh = blockIdx.x / p.nsplit;  // one 32-row query block per head (S_q = 1)
+
+  const char* qh;
+  const char* kh;
+  const char* vh;
+  uint32_t k_rs = ROW, v_rs = ROW, k_bytes, v_bytes;
+  if constexpr (STRIDED) {
+    const int b = bh / p.H, hh = bh - b * p.H;
+    qh = (const char*)p.q + (b * p.qsb + hh * p.qsh) * 2;
+    kh = (const char*)p.k + (b * p.ksb + hh * p.ksh) * 2;
+    vh = (const char*)p.v + (b * p.vsb + hh * p.vsh) * 2;
+    k_rs = p.k_rs;
+    v_rs = p.v_rs;
+    k_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * k_rs + ROW : 0u;
+    v_bytes = p.Sk > 0 ? (uint32_t)(p.Sk - 1) * v_rs + ROW : 0u;
+  } else {
+    qh = (const char*)p.q + (size_t)bh * D * 2;
+    kh = (const char*)p.k + (size_t)bh * p.Sk * D * 2;
+    vh = (const char*)p.v + (size_t)bh * p.Sk * D * 2;
+    k_bytes = v_bytes = (uint32_t)p.Sk * ROW;
+  }
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kh, k_bytes), rv = rsrc(vh, v_bytes);
+  const u32x4 qc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(qh, ROW), chunk * 16, 0, 0));
+
+  const int k_begin = split * p.split_tiles * decode_tile_keys(D);
+  const int k_end = min(p.Sk, k_begin + p.split_tiles * decode_tile_keys(D));
+  float m = -__builtin_inff();  // reference max, log2 units (scores times c)
+  float l = 0.f;
+  float o[8] = {};
+  // rows of an iteration starting at r0 (past the split: an offset past the
+  // range, so they read as 0 without touching memory, and are masked)
+  auto load = [&](int r0, u32x4 (&kx)[U], u32x4 (&vx)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + (wave * U + u) * RPI + sub;
+      const bool ok = row < k_end;
+      kx[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rk, ok ? (uint32_t)row * k_rs + chunk * 16 : k_bytes, 0, kDecode1LoadAux));
+      vx[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rv, ok ? (uint32_t)row * v_rs + chunk * 16 : v_bytes, 0, kDecode1LoadAux));
+    }
+  };
+  auto compute = [&](int r0, const u32x4 (&kx)[U], const u32x4 (&vx)[U]) {
+    float x[U];
+    float xm = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + (wave * U + u) * RPI + sub;
+      float sp = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sp = E::dot2(qc[j], kx[u][j], sp);
+      const float sc = group_sum<LPR>(sp);
+      x[u] = row < k_end ? sc * p.c : -__builtin_inff();
+      xm = fmaxf(xm, x[u]);
+    }
+    const bool grow = xm > m + kDec1Margin;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mn = grow ? xm : m;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.f;  // 0 for the first rows (m = -inf)
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] *= alpha;
+      m = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float pu = x[u] != -__builtin_inff() ? __builtin_amdgcn_exp2f(x[u] - m) : 0.f;
+      l += pu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = __builtin_fmaf(pu, E::lo(vx[u][j]), o[2 * j]);
+        o[2 * j + 1] = __builtin_fmaf(pu, E::hi(vx[u][j]), o[2 * j + 1]);
+      }
+    }
+  };
+  // two register buffers: the next iteration's rows load while this one is
+  // computed (an iteration wholly past the split computes masked zeros)
+  u32x4 ka[U], va[U], kb[U], vb[U];
+  load(k_begin, ka, va);
+  for (int r0 = k_begin; r0 < k_end; r0 += 2 * ITER) {
+    load(r0 + ITER, kb, vb);
+    compute(r0, ka, va);
+    load(r0 + 2 * ITER, ka, va);
+    compute(r0 + ITER, kb, vb);
+  }
+
+  // merge the streams: M = max of their references, L = sum 2^(m_s - M) l_s,
+  // O = sum 2^(m_s - M) o_s / L, LSE = (M + log2 L) ln 2
+  const int stream = wave * RPI + sub;
+  if (chunk == 0) {
+    s_m[stream] = m;
+    s_l[stream] = l;
+  }
+  f32x4* dst = (f32x4*)(s_o + stream * D + chunk * 8);
+  dst[0] = f32x4{o[0], o[1], o[2], o[3]};
+  dst[1] = f32x4{o[4], o[5], o[6], o[7]};
+  barrier();
+  if (threadIdx.x < D) {
+    const int col = threadIdx.x;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < STREAMS; ++t) M = fmaxf(M, s_l[t] > 0.f ? s_m[t] : -__builtin_inff());
+    float L = 0.f, acc = 0.f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int t = 0; t < STREAMS; ++t) {
+        const float wt = s_l[t] > 0.f ? __builtin_amdgcn_exp2f(s_m[t] - M) : 0.f;
+        L = __builtin_fmaf(wt, s_l[t], L);
+        acc = __builtin_fmaf(wt, s_o[t * D + col], acc);
+      }
+    }
+    const bool none = !(L > 0.f);
+    const size_t part = (size_t)bh * p.nsplit + split;
+    p.po[part * D + col] = none ? 0.f : acc / L;
+    if (col == 0) p.pl[part] = none ? -__builtin_inff() : (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f;
+  }
+}
+
 // Wavefronts and blocks per wavefront; LDS per work-group is
 // 2 * 32 * NW * BPW * D * 2 bytes (K and V tiles).
 template <int D>
@@ -293,6 +484,10 @@ struct DecodeShape {
 template <typename T, int D, bool CAUSAL, bool TAIL, bool STRIDED>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
   constexpr int NW = DecodeShape<D>::NW, BPW = DecodeShape<D>::BPW;
+  // a single query row at d = 64 / 128 runs decode1_kernel (any mask keeps
+  // every key of it; see launch_decode_s)
+  constexpr bool kDec1 = (D == 64 || D == 128) && !CAUSAL;
+  constexpr int kDec1Unroll = 4;
   DecParams p;
   p.q = a.q;
   p.k = a.k;
@@ -317,8 +512,16 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan, hipStrea
     osb = st[9]; osh = st[10]; osr = st[11];
   }
   const long long grid = (long long)a.B * a.H * plan.nrb * plan.nsplit;
-  hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, TAIL, NW, BPW, STRIDED>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     stream, p);
+  bool one_row = false;
+  if constexpr (kDec1) {
+    if (a.Sq == 1) {
+      one_row = true;
+      hipLaunchKernelGGL((decode1_kernel<T, D, kDec1Unroll, STRIDED>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    }
+  }
+  if (!one_row)
+    hipLaunchKernelGGL((decode_kernel<T, D, CAUSAL, TAIL, NW, BPW, STRIDED>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeParams m;

@@ -82,7 +82,8 @@ constexpr int waves_per_simd() { return D == 64 ? 4 : 2; }
 
 // Variants launched as a persistent grid (see launch_t): d = 128 except the
 // ragged non-causal one, which spilled 100-220 B with the block loop.  At
-// d = 64 the loop cost registers, spills and 15-18 % at S >= 4096.
+// d = 64 the loop spills registers (32-112 B in the non-causal variants; the
+// causal ones lost 15-18 % at S >= 4096).
 template <int D, bool CAUSAL, bool TAIL>
 constexpr bool persistent_variant() { return D == 128 && (CAUSAL || !TAIL); }
 

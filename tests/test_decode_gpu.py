@@ -73,6 +73,38 @@ def test_decode_no_keys():
     assert (o.float() == 0).all().item() and torch.isneginf(lse).all().item()
 
 
+def test_decode_one_row_no_keys():
+    """S_q = 1 (the register-staged kernel) with S_k = 0: O = 0, LSE = -inf."""
+    q = make_inputs_kv(2, 3, 1, 0, 64, "fp16", seed=80_550)[0].cuda()
+    o = torch.full_like(q, float("nan"))
+    lse = torch.zeros(2, 3, 1, device="cuda")
+    need = fa.fa_fwd_decode_workspace_size(2, 3, 1, 0, 64)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    say("decode Sq=1 Sk=0")
+    st = fa.fa_fwd_decode(q.data_ptr(), 0, 0, o.data_ptr(), lse.data_ptr(), 2, 3, 1, 0, 64, 0, 0.125,
+                          fa.FA_DTYPE_FP16, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert (o.float() == 0).all().item() and torch.isneginf(lse).all().item()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_rising_scores(d):
+    """S_q = 1 with scores that climb by about 200 (natural units) along the
+    keys, past what fp32 exponentials hold, so every stream moves its
+    reference max many times and the splits' LSEs differ widely."""
+    q, k, v = make_inputs_kv(2, 4, 1, 6000, d, "bf16", seed=80_650 + d)
+    qf = q.float()
+    ramp = torch.linspace(0.0, 1.0, 6000).view(1, 1, 6000, 1)
+    scale = default_scale(d)
+    # score_j = scale * q.k_j ~ 200 * j / Sk (natural units) on top of the noise
+    k = (k.float() + ramp * qf * (200.0 / (scale * (qf * qf).sum(-1, keepdim=True)))).to(torch.bfloat16)
+    say(f"decode rising d={d}")
+    o, lse = run(q, k, v, False, scale)
+    o_ref, lse_ref = oracle.attention_kv(to64(q), to64(k), to64(v), False, scale, workers=8)
+    compare(o, lse, o_ref, lse_ref, f"decode rising d={d}")
+
+
 def test_decode_scale_zero():
     q, k, v = make_inputs_kv(1, 2, 4, 3000, 64, "bf16", seed=80_600)
     say("decode scale 0")
