@@ -8,6 +8,8 @@ same key split) and within the oracle's tolerances; torch allocates nothing
 during the calls; shapes beyond the array's size are rejected before any
 launch."""
 
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -28,11 +30,16 @@ def _compare(B, H, Sq, Sk, d, dtype, causal, seed):
     o_ref_gpu, l_ref_gpu = fa.decode(qd, kd, vd, causal=causal, scale=scale)
     out = torch.full_like(qd, float("nan"))
     lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device="cuda")
+    # nothing is allocated during the call: the peak stays at the level it
+    # starts from (collected first, so that no earlier test's tensors are
+    # freed meanwhile)
+    gc.collect()
     torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
     before = torch.cuda.memory_allocated()
     fa.decode_noalloc(qd, kd, vd, out, lse, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    assert torch.cuda.memory_allocated() == before
+    assert torch.cuda.max_memory_allocated() == before
     assert torch.equal(out, o_ref_gpu) and torch.equal(lse, l_ref_gpu)
     o_ref, l_ref = oracle.attention_kv(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, scale)
     eo = float(np.abs(out.float().cpu().double().numpy() - o_ref).max())
