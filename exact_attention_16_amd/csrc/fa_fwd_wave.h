@@ -413,18 +413,21 @@ struct FwdWave {
 #pragma unroll
         for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(sacc[sb][r]));
     }
-    // row max as a tree (independent max3 chains, then combined)
-    float mq[4];
+    // row max: two chains over the 16 * SB scores, each step taking two more
+    // (one v_max3 per step; the earlier four-chain tree took 23 instructions
+    // for 32 scores, this takes 17)
+    float mc2[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mq[j] = fmaxf(sacc[0][4 * j], sacc[0][4 * j + 1]);
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int b0 = c2 * 8 * SB;  // first score of this chain (flat index sb * 16 + r)
+      float m = fmaxf(fmaxf(sacc[b0 / 16][b0 % 16], sacc[(b0 + 1) / 16][(b0 + 1) % 16]), sacc[(b0 + 2) / 16][(b0 + 2) % 16]);
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        if (sb == 0 && (r & 3) == 0) continue;
-        mq[r >> 2] = fmaxf(mq[r >> 2], fmaxf(sacc[sb][r], sacc[sb][r + 1]));
-      }
-    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+      for (int i = b0 + 3; i + 1 < b0 + 8 * SB; i += 2)
+        m = fmaxf(fmaxf(m, sacc[i / 16][i % 16]), sacc[(i + 1) / 16][(i + 1) % 16]);
+      if constexpr ((8 * SB - 3) % 2 == 1) m = fmaxf(m, sacc[(b0 + 8 * SB - 1) / 16][(b0 + 8 * SB - 1) % 16]);
+      mc2[c2] = m;
+    }
+    float mx = fmaxf(mc2[0], mc2[1]);
     mx = max_with_partner(mx);
     const float m_new = fmaxf(m_used, mx);
     const bool grow = (m_used == -__builtin_inff()) || (c * (m_new - m_used) > kRescaleMargin);
