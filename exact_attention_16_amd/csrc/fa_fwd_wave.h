@@ -231,6 +231,16 @@ struct FwdWave {
     lsum_o = 0.f;
   }
 
+  // The wavefront index for the load blocks below, made wavefront-uniform so
+  // that each load's LDS destination is a scalar value rather than a vector
+  // register kept live through the step loop.  (Measured on the MI355X:
+  // short_seq_batch +1 %, long_seq_causal +1 %, S >= 4096 causal d = 64
+  // +2 %, the rest within noise; the strided variants keep the plain index,
+  // with which they allocate registers without spilling.)
+  __device__ __forceinline__ int uniform_wave() const {
+    return STRIDED ? wave : __builtin_amdgcn_readfirstlane(wave);
+  }
+
   // HBM -> LDS copies of one key tile (BN rows of K, or of V), issued
   // cooperatively by all NW wavefronts.
   //
@@ -251,7 +261,7 @@ struct FwdWave {
     const uint32_t base = k_row(tile * BN);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int f = i * NW + wave;  // block (sb, kk)
+      const int f = i * NW + uniform_wave();  // block (sb, kk)
       const int ksb = f / KSTEPS, kk = f % KSTEPS;
       const uint32_t off = base + k_row(ksb * 32 + (lane & 31)) + (kk * 2 + (lane >> 5)) * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + f * 1024), 16, off, 0, 0, 0);
@@ -268,7 +278,7 @@ struct FwdWave {
     const int vcol = x * 32 + (vg & 1) * 16 + (lp & 1) * 8;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int f = i * NW + wave;  // block ((sb * 2 + cc) * 2 + tt) * (DB / 2) + dp
+      const int f = i * NW + uniform_wave();  // block ((sb * 2 + cc) * 2 + tt) * (DB / 2) + dp
       const int dp = f % (DB / 2), rest = f / (DB / 2);
       const uint32_t off = base + v_row(rest * 8 + vrow) + (dp * 64 + vcol) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + f * 1024), 16, off, 0, 0, 0);
