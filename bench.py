@@ -40,10 +40,13 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 RIDGE = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
+# The recorded HBM counters belong to one binary: its kernel sources and the
+# build script that holds the compiler flags.
+BUILD_SCRIPT = os.path.join(ROOT, "exact_attention_16_amd", "build.py")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
-                  for f in ("fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")]
+                  for f in ("fa_fwd.hip", "fa_fwd_wide.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")] + [BUILD_SCRIPT]
 DECODE_SOURCES = [os.path.join(ROOT, "exact_attention_16_amd", "csrc", f)
-                  for f in ("fa_decode.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")]
+                  for f in ("fa_decode.hip", "fa_fwd_wave.h", "fa_device.h", "fa_launch.h")] + [BUILD_SCRIPT]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_fa_fwd.md")
 DECODE_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "hbm_traffic_fa_decode.md")
 
